@@ -1,0 +1,325 @@
+// Exported C ABI of libmoesparse: argument validation, the launch plan, the
+// workspace layout and the kernel sequence of each call.
+//
+// Every check that can fail on the host runs before the first HIP call, so a
+// bad call is reported without touching a device.  No call allocates memory,
+// synchronises the host or issues a memset (zeroing, where needed, is done by
+// kernels), so calls can be captured in a HIP graph.
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
+{
+    if (!s || !p) return MOE_ERR_INVALID_ARG;
+    const bool calib = calib_tokens > 0;
+    if (!calib && mode != MOE_SPARSE && mode != MOE_DENSE) return MOE_ERR_INVALID_ARG;
+    const int T = calib ? calib_tokens : s->T;
+    if (T < 0 || s->H <= 0 || s->E <= 0 || s->I <= 0 || s->K <= 0 || s->K > s->E || s->S < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (s->S > 0 && s->I_shared <= 0) return MOE_ERR_INVALID_ARG;
+    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID_ARG;
+    if (s->K > kMaxK) return MOE_ERR_UNSUPPORTED;
+
+    memset(p, 0, sizeof *p);
+    p->T = T;
+    p->H = s->H;
+    p->E = s->E;
+    p->I = s->I;
+    p->K = s->K;
+    p->S = s->S;
+    p->Is = s->S > 0 ? s->I_shared : 0;
+    p->dtype = s->dtype;
+    p->renorm = s->renormalize;
+    p->epl = s->dtype == MOE_BF16 ? 8 : 4;
+    if (p->H % (kWave * p->epl) != 0) return MOE_ERR_UNSUPPORTED;
+    p->NS = p->H / (kWave * p->epl);
+    if (p->NS != 1 && p->NS != 2 && p->NS != 4 && p->NS != 8 && p->NS != 16) return MOE_ERR_UNSUPPORTED;
+    if (p->I % 32 != 0 || p->I > kMaxRows) return MOE_ERR_UNSUPPORTED;
+    if (p->S > 0 && (p->Is % 32 != 0 || p->Is > kMaxRows)) return MOE_ERR_UNSUPPORTED;
+    if (p->E + p->S > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    // sizes that index device buffers must fit the kernels' int arithmetic
+    const long long P_ll = (long long)T * (s->K + s->S);
+    if (P_ll > INT_MAX / 64) return MOE_ERR_UNSUPPORTED;
+
+    p->Imax = (p->S > 0 && p->Is > p->I) ? p->Is : p->I;
+    p->W = p->Imax / 32;
+    p->slots = p->K + p->S;
+    p->A = T * p->K;
+    p->P = T * p->slots;
+    p->EX = p->E + p->S;
+    p->max_touched = T > 0 ? (p->A < p->E ? p->A : p->E) + p->S : 0;
+
+    // rows per projection workgroup: the smallest multiple of 32 that keeps the
+    // grid at or below ~2048 workgroups (8 per CU on 256 CUs)
+    p->R = 32;
+    while (p->R < kMaxRowsPerChunk &&
+           (long long)p->max_touched * ((p->Imax + p->R - 1) / p->R) > 2048)
+        p->R += 32;
+    p->C = (p->Imax + p->R - 1) / p->R;
+
+    // token tile: covers the mean pairs per touched routed expert, bounded by
+    // the registers the hidden-state tile takes (TT * NS vectors <= 32)
+    const int touched_routed = p->A < p->E ? p->A : p->E;
+    const int mean_ne = touched_routed > 0 ? (p->A + touched_routed - 1) / touched_routed : 1;
+    const int tt_cap = p->NS <= 4 ? 8 : (p->NS == 8 ? 4 : 2);
+    p->TT = 1;
+    while (p->TT < mean_ne && p->TT < tt_cap) p->TT *= 2;
+
+    // down projection: column tiles of 64 lanes x 16 bytes; split the union
+    // rows so the grid has ~1024 workgroups when few experts are touched
+    p->NCT = p->NS;
+    const long long base = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT;
+    long long split = (1024 + base - 1) / base;
+    if (split > 32) split = 32;
+    if (split < 1) split = 1;
+    p->NSPLIT = (int)split;
+
+    // workspace layout
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    p->off_ids = take((size_t)p->A * 4);
+    p->off_w = take((size_t)p->A * 4);
+    p->off_hdr = take(64 * 4);
+    p->off_counts = take((size_t)p->EX * 4);
+    p->off_offsets = take((size_t)(p->EX + 1) * 4);
+    p->off_touched = take((size_t)p->EX * 4);
+    p->off_pair_tok = take((size_t)p->P * 4);
+    p->off_pair_slot = take((size_t)p->P * 4);
+    p->off_pos = take((size_t)p->P * 4);
+    p->off_union = take((size_t)p->EX * p->W * 4);
+    p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
+    p->off_partial = take(calib ? 0 : (size_t)p->NSPLIT * p->P * p->H * 4);
+    p->off_taus = take((size_t)(2 + p->EX) * 4);
+    p->total = o;
+    return MOE_OK;
+}
+
+static bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+template <class T>
+static T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_status_string(int32_t status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument (NULL pointer, bad size, bad enum, q outside [0,1] or misaligned pointer)";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside what the kernels implement";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than required";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch or runtime call failed";
+    }
+    return "unknown moe_status";
+}
+
+moe_status moe_workspace_size(const moe_shape *shape, int32_t mode, size_t *bytes)
+{
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    Plan pl;
+    const moe_status st = make_plan(shape, mode, 0, &pl);
+    if (st != MOE_OK) return st;
+    *bytes = pl.total;
+    return MOE_OK;
+}
+
+moe_status moe_calibrate_workspace_size(const moe_shape *shape, int32_t Tc, size_t *bytes)
+{
+    if (!bytes || Tc <= 0) return MOE_ERR_INVALID_ARG;
+    Plan pl;
+    const moe_status st = make_plan(shape, MOE_SPARSE, Tc, &pl);
+    if (st != MOE_OK) return st;
+    *bytes = pl.total;
+    return MOE_OK;
+}
+
+moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t K, int32_t renormalize,
+                          int32_t *topk_ids, float *topk_w, void *hip_stream)
+{
+    if (T < 0 || E <= 0 || K <= 0 || K > E || (renormalize != 0 && renormalize != 1))
+        return MOE_ERR_INVALID_ARG;
+    if (K > kMaxK || E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+    return launch_route(logits, T, E, K, renormalize, topk_ids, topk_w, (hipStream_t)hip_stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+}
+
+moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe_ffn_args *a,
+                                 void *hip_stream)
+{
+    if (!shape || !a) return MOE_ERR_INVALID_ARG;
+    Plan pl;
+    moe_status st = make_plan(shape, mode, 0, &pl);
+    if (st != MOE_OK) return st;
+    if (pl.T == 0) return MOE_OK;
+    if (!a->x || !a->router_logits || !a->w_gate || !a->w_up || !a->w_down || !a->y || !a->workspace)
+        return MOE_ERR_INVALID_ARG;
+    if (pl.S > 0 && (!a->ws_gate || !a->ws_up || !a->ws_down)) return MOE_ERR_INVALID_ARG;
+    if (mode == MOE_SPARSE && !a->tau) return MOE_ERR_INVALID_ARG;
+    const void *a16[] = {a->x, a->w_gate, a->w_up, a->w_down, a->y};
+    for (const void *ptr : a16)
+        if (!aligned(ptr, 16)) return MOE_ERR_INVALID_ARG;
+    if (pl.S > 0 && (!aligned(a->ws_gate, 16) || !aligned(a->ws_up, 16) || !aligned(a->ws_down, 16)))
+        return MOE_ERR_INVALID_ARG;
+    const void *a4[] = {a->router_logits, a->tau, a->mask_bits, a->union_idx, a->union_cnt, a->topk_ids, a->topk_w};
+    for (const void *ptr : a4)
+        if (ptr && !aligned(ptr, 4)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(a->workspace, 256)) return MOE_ERR_INVALID_ARG;
+    if (a->workspace_bytes < pl.total) return MOE_ERR_WORKSPACE;
+
+    hipStream_t stream = (hipStream_t)hip_stream;
+    void *ws = a->workspace;
+    int32_t *ids = a->topk_ids ? a->topk_ids : ws_at<int32_t>(ws, pl.off_ids);
+    float *w = a->topk_w ? a->topk_w : ws_at<float>(ws, pl.off_w);
+    int32_t *hdr = ws_at<int32_t>(ws, pl.off_hdr);
+    int32_t *counts = ws_at<int32_t>(ws, pl.off_counts);
+    int32_t *offsets = ws_at<int32_t>(ws, pl.off_offsets);
+    int32_t *touched = ws_at<int32_t>(ws, pl.off_touched);
+    int32_t *pair_tok = ws_at<int32_t>(ws, pl.off_pair_tok);
+    int32_t *pair_slot = ws_at<int32_t>(ws, pl.off_pair_slot);
+    int32_t *pos = ws_at<int32_t>(ws, pl.off_pos);
+    uint32_t *union_words = ws_at<uint32_t>(ws, pl.off_union);
+    float *h = ws_at<float>(ws, pl.off_h);
+    float *partial = ws_at<float>(ws, pl.off_partial);
+
+    if (launch_route(a->router_logits, pl.T, pl.E, pl.K, pl.renorm, ids, w, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+
+    GroupParams gp{};
+    gp.ids = ids;
+    gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
+    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
+    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos;
+    gp.union_cnt = a->union_cnt;
+    if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    ProjParams pp{};
+    pp.x = a->x; pp.wg = a->w_gate; pp.wu = a->w_up; pp.swg = a->ws_gate; pp.swu = a->ws_up;
+    pp.tau = a->tau;
+    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched;
+    pp.pair_tok = pair_tok; pp.pair_slot = pair_slot;
+    pp.h = h; pp.mask_bits = a->mask_bits; pp.union_words = union_words;
+    pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
+    pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
+    if (a->prof_event_begin && hipEventRecord((hipEvent_t)a->prof_event_begin, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_proj(pl, pp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (a->prof_event_end && hipEventRecord((hipEvent_t)a->prof_event_end, stream) != hipSuccess)
+        return MOE_ERR_HIP;
+
+    DownParams dp{};
+    dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
+    dp.hdr = hdr; dp.counts = counts; dp.offsets = offsets; dp.touched = touched;
+    dp.union_words = union_words; dp.partial = partial;
+    dp.union_idx = a->union_idx; dp.union_cnt = a->union_cnt;
+    dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
+    dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.NSPLIT = pl.NSPLIT;
+    if (launch_down(pl, dp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    CombineParams cp{};
+    cp.partial = partial; cp.topk_w = w; cp.pos = pos; cp.y = a->y;
+    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NSPLIT = pl.NSPLIT;
+    if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, const float *logits_calib,
+                                   int32_t Tc, const void *w_gate, const void *ws_gate, float q,
+                                   int32_t per_expert, float *tau_out, void *workspace,
+                                   size_t workspace_bytes, void *hip_stream)
+{
+    if (!shape || Tc <= 0) return MOE_ERR_INVALID_ARG;
+    if (!(q >= 0.f && q <= 1.f)) return MOE_ERR_INVALID_ARG;  // also rejects NaN
+    if (per_expert != 0 && per_expert != 1) return MOE_ERR_INVALID_ARG;
+    Plan pl;
+    moe_status st = make_plan(shape, MOE_SPARSE, Tc, &pl);
+    if (st != MOE_OK) return st;
+    if (!x_calib || !logits_calib || !w_gate || !tau_out || !workspace) return MOE_ERR_INVALID_ARG;
+    if (pl.S > 0 && !ws_gate) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x_calib, 16) || !aligned(w_gate, 16) || (pl.S > 0 && !aligned(ws_gate, 16)))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(logits_calib, 4) || !aligned(tau_out, 4) || !aligned(workspace, 256))
+        return MOE_ERR_INVALID_ARG;
+    if (workspace_bytes < pl.total) return MOE_ERR_WORKSPACE;
+
+    hipStream_t stream = (hipStream_t)hip_stream;
+    int32_t *ids = ws_at<int32_t>(workspace, pl.off_ids);
+    float *w = ws_at<float>(workspace, pl.off_w);
+    int32_t *hdr = ws_at<int32_t>(workspace, pl.off_hdr);
+    int32_t *counts = ws_at<int32_t>(workspace, pl.off_counts);
+    int32_t *offsets = ws_at<int32_t>(workspace, pl.off_offsets);
+    int32_t *touched = ws_at<int32_t>(workspace, pl.off_touched);
+    int32_t *pair_tok = ws_at<int32_t>(workspace, pl.off_pair_tok);
+    int32_t *pair_slot = ws_at<int32_t>(workspace, pl.off_pair_slot);
+    int32_t *pos = ws_at<int32_t>(workspace, pl.off_pos);
+    float *scores = ws_at<float>(workspace, pl.off_h);
+    float *taus = ws_at<float>(workspace, pl.off_taus);
+
+    if (launch_route(logits_calib, pl.T, pl.E, pl.K, 1, ids, w, stream) != hipSuccess) return MOE_ERR_HIP;
+    GroupParams gp{};
+    gp.ids = ids;
+    gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
+    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
+    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos; gp.union_cnt = nullptr;
+    if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    ProjParams pp{};
+    pp.x = x_calib; pp.wg = w_gate; pp.wu = w_gate; pp.swg = ws_gate; pp.swu = ws_gate;
+    pp.tau = nullptr;
+    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched;
+    pp.pair_tok = pair_tok; pp.pair_slot = pair_slot;
+    pp.h = scores; pp.mask_bits = nullptr; pp.union_words = nullptr;
+    pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
+    pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
+    if (launch_proj(pl, pp, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
+
+    SelectParams sp{};
+    sp.scores = scores; sp.counts = counts; sp.offsets = offsets; sp.taus = taus; sp.q = q;
+    sp.E = pl.E; sp.I = pl.I; sp.Is = pl.Is; sp.S = pl.S; sp.A = pl.A; sp.T = pl.T; sp.EX = pl.EX;
+    sp.per_expert = per_expert;
+    if (launch_select(pl, sp, tau_out, stream) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_timer_create(void **event)
+{
+    if (!event) return MOE_ERR_INVALID_ARG;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return MOE_ERR_HIP;
+    *event = (void *)e;
+    return MOE_OK;
+}
+
+moe_status moe_timer_destroy(void *event)
+{
+    if (!event) return MOE_ERR_INVALID_ARG;
+    return hipEventDestroy((hipEvent_t)event) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_timer_elapsed_ms(void *begin, void *end, float *ms)
+{
+    if (!begin || !end || !ms) return MOE_ERR_INVALID_ARG;
+    if (hipEventSynchronize((hipEvent_t)end) != hipSuccess) return MOE_ERR_HIP;
+    return hipEventElapsedTime(ms, (hipEvent_t)begin, (hipEvent_t)end) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+// Down projection over an expert's active neurons, and the top-K weighted
+// combine.
+//
+// gist.science page of arXiv 2605.08575, Technical Summary, Methodology,
+// "Fused Up-Down Projection": only active neurons' weights are gathered.  With
+// the down matrix stored neuron-major, an active neuron is one contiguous row
+// of H elements and an inactive one is never read.
+//
+// k_down: one workgroup per (touched expert, column tile, split).  It expands
+// the expert's union bit words into an ascending row list in LDS (popcount
+// prefix), takes its split of that list, and accumulates
+//     o[pair, cols] += h[row][pair] * w_down[row][cols]
+// for every pair of the expert in register tiles of TB tokens.  The 4
+// wavefronts take interleaved rows of the split and are summed through LDS in
+// a fixed order; splits land in separate partial buffers that the combine
+// kernel adds in a fixed order, so no floating-point atomics are used and the
+// result is bitwise reproducible.
+#include "moe_internal.h"
+
+namespace moe {
+
+template <class Tr, int TB, int MODE>
+__global__ __launch_bounds__(256) void k_down(DownParams p)
+{
+    using V = typename Tr::V;
+    constexpr int EPL = Tr::kEpl;
+    constexpr int UR = 4;  // rows in flight per wavefront
+    __shared__ uint16_t s_list[kMaxRows];
+    __shared__ int s_wpre[kMaxRows / 32 + 1];
+    __shared__ float s_red[3][TB][kWave * EPL];
+
+    const int per_e = p.NCT * p.NSPLIT;
+    const int s = blockIdx.x / per_e;
+    const int rem = blockIdx.x - s * per_e;
+    const int ct = rem / p.NSPLIT;
+    const int sp = rem - ct * p.NSPLIT;
+    if (s >= p.hdr[0]) return;
+    const int xe = p.touched[s];
+    const bool shared = xe >= p.E;
+    const int Ie = shared ? p.Is : p.I;
+    const int n = p.counts[xe];
+    const int off = p.offsets[xe];
+    const int rowV = p.NCT * kWave;
+    const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
+    const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat;
+    const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+
+    // ---- union row list -----------------------------------------------------
+    int U;
+    if (MODE == MOE_DENSE) {
+        U = Ie;
+    } else {
+        const int nw = Ie / 32;
+        const uint32_t *uw = p.union_words + (size_t)xe * p.W;
+        // popcount prefix over the words: thread i owns words [i*per, i*per+per)
+        const int per = (nw + blockDim.x - 1) / blockDim.x;
+        const int w_begin = threadIdx.x * per;
+        int cnt = 0;
+        for (int i = 0; i < per; ++i)
+            if (w_begin + i < nw) cnt += __popc(uw[w_begin + i]);
+        // block exclusive scan of cnt (256 threads, 4 wavefronts)
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += o;
+        }
+        if (lane == kWave - 1) s_wpre[wave] = incl;
+        __syncthreads();
+        int wbase = 0;
+        for (int i = 0; i < wave; ++i) wbase += s_wpre[i];
+        U = s_wpre[0] + s_wpre[1] + s_wpre[2] + s_wpre[3];
+        int pos = wbase + incl - cnt;
+        for (int i = 0; i < per; ++i) {
+            const int wd = w_begin + i;
+            if (wd >= nw) break;
+            uint32_t bits = uw[wd];
+            while (bits) {
+                const int b = __ffs(bits) - 1;
+                bits &= bits - 1;
+                s_list[pos++] = (uint16_t)(wd * 32 + b);
+            }
+        }
+        __syncthreads();
+    }
+    if (ct == 0 && sp == 0) {
+        if (p.union_idx)
+            for (int i = threadIdx.x; i < U; i += blockDim.x)
+                p.union_idx[(size_t)xe * p.Imax + i] = (MODE == MOE_DENSE) ? i : (int)s_list[i];
+        if (p.union_cnt && threadIdx.x == 0) p.union_cnt[xe] = U;
+    }
+
+    const int lo = (int)(((long long)U * sp) / p.NSPLIT);
+    const int hi = (int)(((long long)U * (sp + 1)) / p.NSPLIT);
+    const int cv = ct * kWave + lane;  // this lane's vector of each row
+
+    for (int t0 = 0; t0 < n; t0 += TB) {
+        const int nt = min(TB, n - t0);
+        float acc[TB][EPL];
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+
+        for (int ib = lo + wave; ib < hi; ib += 4 * UR) {
+            V wv[UR];
+            float hv[UR][TB];
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                const int i = ib + 4 * u;
+                const int j = (i < hi) ? ((MODE == MOE_DENSE) ? i : (int)s_list[i]) : -1;
+                wv[u] = (j >= 0) ? Wd[(size_t)j * rowV + cv] : Tr::zero();
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+                    hv[u][t] = (j >= 0 && t < nt) ? hb[(size_t)j * n + t0 + t] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < UR; ++u) {
+                float wf[EPL];
+                Tr::unpack(wv[u], wf);
+#pragma unroll
+                for (int t = 0; t < TB; ++t)
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[t][e] = fmaf(hv[u][t], wf[e], acc[t][e]);
+            }
+        }
+
+        // sum the 4 wavefronts in a fixed order: wave 0 + (1 + (2 + 3))... via LDS
+        __syncthreads();
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s_red[wave - 1][t][lane * EPL + e] = acc[t][e];
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                if (t >= nt) break;
+                float o[EPL];
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    o[e] = acc[t][e] + s_red[0][t][lane * EPL + e] + s_red[1][t][lane * EPL + e] +
+                           s_red[2][t][lane * EPL + e];
+                float *dst = p.partial + ((size_t)sp * p.P + off + t0 + t) * p.H + (size_t)cv * EPL;
+#pragma unroll
+                for (int e = 0; e < EPL; e += 4)
+                    *reinterpret_cast<float4 *>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+            }
+        }
+    }
+}
+
+template <class Tr, int TB>
+static hipError_t launch_down_t(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+{
+    const dim3 grid(pl.max_touched * pl.NCT * pl.NSPLIT), block(256);
+    if (mode == MOE_DENSE) hipLaunchKernelGGL((k_down<Tr, TB, MOE_DENSE>), grid, block, 0, st, dp);
+    else hipLaunchKernelGGL((k_down<Tr, TB, MOE_SPARSE>), grid, block, 0, st, dp);
+    return hipGetLastError();
+}
+
+template <class Tr>
+static hipError_t launch_down_tr(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+{
+    switch (pl.TT) {
+    case 1: return launch_down_t<Tr, 1>(pl, dp, mode, st);
+    case 2: return launch_down_t<Tr, 2>(pl, dp, mode, st);
+    case 4: return launch_down_t<Tr, 4>(pl, dp, mode, st);
+    case 8: return launch_down_t<Tr, 8>(pl, dp, mode, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+{
+    if (pl.T <= 0) return hipSuccess;
+    return pl.dtype == MOE_BF16 ? launch_down_tr<BF16>(pl, dp, mode, st)
+                                : launch_down_tr<F32>(pl, dp, mode, st);
+}
+
+// ---------------------------------------------------------------------------
+// k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)],
+// each o being the fixed-order sum of the NSPLIT partials.  One thread per 4
+// columns of one token.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(CombineParams p)
+{
+    const int t = blockIdx.x;
+    const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
+    const int H4 = p.H / 4;
+    if (c4 >= H4) return;
+    float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < p.slots; ++k) {
+        const int pr = p.pos[(size_t)t * p.slots + k];
+        const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < p.NSPLIT; ++sp) {
+            const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)sp * p.P + pr) * p.H)[c4];
+            o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+        }
+        y.x = fmaf(wk, o.x, y.x);
+        y.y = fmaf(wk, o.y, y.y);
+        y.z = fmaf(wk, o.z, y.z);
+        y.w = fmaf(wk, o.w, y.w);
+    }
+    reinterpret_cast<float4 *>(p.y + (size_t)t * p.H)[c4] = y;
+}
+
+hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t st)
+{
+    if (pl.T <= 0) return hipSuccess;
+    const int H4 = pl.H / 4;
+    hipLaunchKernelGGL(k_combine, dim3(pl.T, (H4 + 255) / 256), dim3(256), 0, st, cp);
+    return hipGetLastError();
+}
+
+}  // namespace moe

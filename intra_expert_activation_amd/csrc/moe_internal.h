@@ -1,0 +1,187 @@
+// Internal definitions of libmoesparse: the launch plan, workspace carving,
+// kernel parameter blocks and small device helpers.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_sparse.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 512;   // E + S
+constexpr int kMaxK = 32;
+constexpr int kMaxRows = 16384;    // I, I_shared
+constexpr int kMaxRowsPerChunk = 256;
+
+// ---------------------------------------------------------------------------
+// Launch plan: every size a kernel grid or the workspace depends on.  It is a
+// pure function of the shape (never of the data), so a call can be captured in
+// a graph and the workspace size is known before the call.
+// ---------------------------------------------------------------------------
+struct Plan {
+    int T, H, E, I, K, S, Is, dtype, renorm;
+    int Imax;        // max(I, I_shared)
+    int W;           // mask words per (token, slot) row = Imax / 32
+    int slots;       // K + S
+    int A;           // routed pairs T*K
+    int P;           // all pairs T*(K+S)
+    int EX;          // experts E + S
+    int epl;         // elements per 16-byte vector (8 bf16, 4 f32)
+    int NS;          // 16-byte vectors per lane per row: H / (64 * epl)
+    int max_touched; // upper bound on experts with at least one pair
+    // expert projection kernel (gate, score, mask, up)
+    int R;           // neuron rows per workgroup (multiple of 32, <= 256)
+    int C;           // row chunks per expert: ceil(Imax / R)
+    int TT;          // tokens per register tile
+    // down projection kernel
+    int NCT;         // column tiles: H / (64 * epl)
+    int NSPLIT;      // splits of an expert's union rows (deterministic split-K)
+    // workspace layout (byte offsets)
+    size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched;
+    size_t off_pair_tok, off_pair_slot, off_pos, off_union, off_h, off_partial;
+    size_t off_taus;
+    size_t total;
+};
+
+// Validates a shape; fills the plan.  calib_tokens > 0 plans a calibration
+// (score) pass over that many tokens instead of a forward pass.
+moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p);
+
+// ---------------------------------------------------------------------------
+// Kernel parameter blocks
+// ---------------------------------------------------------------------------
+struct GroupParams {
+    const int32_t *ids;   // [T,K]
+    int T, K, E, S, A, P, slots;
+    int32_t *hdr;         // [0] = number of touched experts
+    int32_t *counts;      // [EX]
+    int32_t *offsets;     // [EX+1]
+    int32_t *touched;     // [EX], ascending expert ids with count > 0
+    int32_t *pair_tok;    // [P] token of the pair at each grouped position
+    int32_t *pair_slot;   // [P] slot of the pair
+    int32_t *pos;         // [T*slots] grouped position of (t, slot)
+    int32_t *union_cnt;   // optional output, zeroed for untouched experts
+};
+
+struct ProjParams {
+    const void *x;
+    const void *wg, *wu, *swg, *swu;
+    const float *tau;
+    const int32_t *hdr, *counts, *offsets, *touched, *pair_tok, *pair_slot;
+    float *h;             // per-expert blocks [rows][n_e] (fp32)
+    uint32_t *mask_bits;  // optional output [T,slots,W]
+    uint32_t *union_words;// [EX,W]
+    int H, E, I, Is, S, K, A, W, slots, C, R;
+};
+
+struct DownParams {
+    const void *wd, *swd;
+    const float *h;
+    const int32_t *hdr, *counts, *offsets, *touched;
+    const uint32_t *union_words;
+    float *partial;       // [NSPLIT, P, H]
+    int32_t *union_idx;   // optional output [EX, Imax]
+    int32_t *union_cnt;   // optional output [EX]
+    int H, E, I, Is, S, A, P, W, Imax, NCT, NSPLIT;
+};
+
+struct CombineParams {
+    const float *partial;
+    const float *topk_w;
+    const int32_t *pos;
+    float *y;
+    int T, H, K, slots, P, NSPLIT;
+};
+
+struct SelectParams {
+    const float *scores;  // |SiLU| per (pair, neuron), expert blocks as ProjParams::h
+    const int32_t *counts, *offsets;
+    float *taus;          // [2 + EX]: routed, shared, then per expert
+    float q;
+    int E, I, Is, S, A, T, EX, per_expert;
+};
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (each enqueues on `stream` and returns hipGetLastError)
+// ---------------------------------------------------------------------------
+hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,
+                        float *w, hipStream_t stream);
+hipError_t launch_group(const GroupParams &gp, hipStream_t stream);
+// mode: MOE_SPARSE, MOE_DENSE, or kModeScore (calibration scores)
+constexpr int kModeScore = 2;
+hipError_t launch_proj(const Plan &pl, const ProjParams &pp, int mode, hipStream_t stream);
+hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream_t stream);
+hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t stream);
+hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 weights/activations: 8 elements per 16-byte vector.
+struct BF16 {
+    using V = uint4;
+    static constexpr int kEpl = 8;
+    // acc + sum_i w_i * x_i over the 8 lanes of the vector (fp32 accumulate)
+    static __device__ __forceinline__ float dot(V w, V x, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x),
+                                              __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y),
+                                              __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z),
+                                              __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w),
+                                              __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+        return acc;
+    }
+    static __device__ __forceinline__ void unpack(V w, float (&f)[8]) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(u[i] << 16);
+            f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ V zero() { return make_uint4(0, 0, 0, 0); }
+};
+
+// fp32 weights/activations: 4 elements per 16-byte vector.
+struct F32 {
+    using V = float4;
+    static constexpr int kEpl = 4;
+    static __device__ __forceinline__ float dot(V w, V x, float acc) {
+        acc = fmaf(w.x, x.x, acc);
+        acc = fmaf(w.y, x.y, acc);
+        acc = fmaf(w.z, x.z, acc);
+        acc = fmaf(w.w, x.w, acc);
+        return acc;
+    }
+    static __device__ __forceinline__ void unpack(V w, float (&f)[4]) {
+        f[0] = w.x; f[1] = w.y; f[2] = w.z; f[3] = w.w;
+    }
+    static __device__ __forceinline__ V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// SiLU(g) = g * sigmoid(g).  exp(-g) overflows to +inf for g < -88, giving
+// g / inf = -0, the correct limit.
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int lane = threadIdx.x & (kWave - 1);
+    return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+#endif  // __HIPCC__
+
+}  // namespace moe

@@ -1,0 +1,254 @@
+// Routing (softmax + top-K) and token-to-expert grouping (histogram, prefix
+// sum, stable permutation) for the routed MoE layer.
+//
+// The router itself is unchanged by the method (gist.science page of arXiv
+// 2605.08575, Technical Summary, Methodology: router logic preserved); the
+// grouping is what lets every expert process its tokens as one batch.
+#include "moe_internal.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// k_route: one wavefront per token.  Each lane holds up to 8 logits (E <= 512).
+// K rounds of a wavefront arg-max pick the experts in descending logit order
+// (ties to the lower id); softmax weights are exp(l - max) / sum exp(l - max).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E,
+                                               int K, int renorm, int32_t *__restrict__ ids,
+                                               float *__restrict__ w)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    if (t >= T) return;
+    const float *l = logits + (size_t)t * E;
+    constexpr int kPer = kMaxExperts / kWave;
+    float v[kPer];      // ranking value (NaN ranks as -inf)
+    float raw[kPer];    // logit as given
+    uint32_t avail = 0; // bit i: expert lane + 64 i is present and not yet chosen
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + kWave * i;
+        raw[i] = e < E ? l[e] : 0.f;
+        v[i] = (e < E && !isnan(raw[i])) ? raw[i] : -INFINITY;
+        if (e < E) avail |= 1u << i;
+    }
+    // maximum over the non-NaN logits, for a range-safe softmax
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((avail >> i) & 1u) m = fmaxf(m, v[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+    float denom = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((avail >> i) & 1u) denom += expf(raw[i] - m);
+    denom = wave_sum(denom);
+
+    float chosen_e = 0.f;  // lane k keeps exp(l - m) of slot k
+    float sel_sum = 0.f;
+    for (int k = 0; k < K; ++k) {
+        // lane-local best available expert
+        float bv = -INFINITY;
+        int bid = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane + kWave * i;
+            if (((avail >> i) & 1u) && (bid == 0x7fffffff || v[i] > bv)) {
+                bv = v[i];
+                bid = e;
+            }
+        }
+        // wavefront arg-max: larger value, then lower id
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1) {
+            const float ov = __shfl_xor(bv, s, kWave);
+            const int oid = __shfl_xor(bid, s, kWave);
+            if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > bv || (ov == bv && oid < bid))) {
+                bv = ov;
+                bid = oid;
+            }
+        }
+        if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
+        const float ev = expf(l[bid] - m);  // the chosen logit, as given
+        if (lane == k) chosen_e = ev;
+        sel_sum += ev;
+        if (lane == 0) ids[(size_t)t * K + k] = bid;
+    }
+    if (lane < K) {
+        const float p = chosen_e / denom;
+        w[(size_t)t * K + lane] = renorm ? chosen_e / sel_sum : p;
+    }
+}
+
+hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,
+                        float *w, hipStream_t stream)
+{
+    if (T <= 0) return hipSuccess;
+    const int waves = 4;
+    hipLaunchKernelGGL(k_route, dim3((T + waves - 1) / waves), dim3(waves * kWave), 0, stream,
+                       logits, T, E, K, renorm, ids, w);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k_group: one workgroup of 16 wavefronts.  Routed assignments a = t*K + k are
+// ordered by expert, and within an expert by a (a stable counting sort):
+//   pass 1  each wavefront counts its contiguous segment per expert;
+//   scan    per-expert totals, per-wavefront bases, exclusive prefix over
+//           experts, the ascending list of touched experts;
+//   pass 2  each wavefront re-walks its segment and scatters.
+// Lanes holding the same expert are found with one ballot per id bit; their
+// leader updates the per-wavefront counter with an LDS atomic and shares the
+// old value, so the rank inside a 64-assignment chunk is a popcount.
+// The S shared experts follow the routed pairs: pair A + s*T + t.
+// ---------------------------------------------------------------------------
+constexpr int kGroupWaves = 16;
+
+__device__ __forceinline__ uint64_t peers_of(int e, bool valid)
+{
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {  // ids < 512
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return valid ? m : 0ull;
+}
+
+__global__ __launch_bounds__(1024) void k_group(GroupParams p)
+{
+    __shared__ int s_cnt[kGroupWaves][kMaxExperts];
+    __shared__ int s_off[kMaxExperts + 1];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wv = tid / kWave;
+    const int EX = p.E + p.S;
+
+    for (int i = tid; i < kGroupWaves * kMaxExperts; i += blockDim.x) (&s_cnt[0][0])[i] = 0;
+    __syncthreads();
+
+    const int chunks = (p.A + kWave - 1) / kWave;
+    const int per_wave = (chunks + kGroupWaves - 1) / kGroupWaves;
+    const int a_begin = wv * per_wave * kWave;
+    const int a_end = min(p.A, (wv + 1) * per_wave * kWave);
+
+    // pass 1: per-wavefront counts
+    for (int base = a_begin; base < a_end; base += kWave) {
+        const int a = base + lane;
+        const bool valid = a < a_end;
+        const int e = valid ? p.ids[a] : 0;
+        const uint64_t peers = peers_of(e, valid);
+        if (valid && (__ffsll((long long)peers) - 1) == lane) atomicAdd(&s_cnt[wv][e], __popcll(peers));
+    }
+    __syncthreads();
+
+    // per-expert totals; s_cnt becomes the per-wavefront base inside the expert
+    for (int e = tid; e < EX; e += blockDim.x) {
+        int run = 0;
+        if (e < p.E) {
+            for (int w2 = 0; w2 < kGroupWaves; ++w2) {
+                const int c = s_cnt[w2][e];
+                s_cnt[w2][e] = run;
+                run += c;
+            }
+        } else {
+            run = p.T;  // a shared expert serves every token
+        }
+        s_off[e] = run;  // total for now
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // exclusive prefix over experts: lane l owns experts [8l, 8l+8)
+        constexpr int kPer = kMaxExperts / kWave;
+        int loc[kPer];
+        int sum = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            loc[i] = e < EX ? s_off[e] : 0;
+            sum += loc[i];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(incl, s, kWave);
+            if (lane >= s) incl += o;
+        }
+        int run = incl - sum;
+        int ntouched_before = 0;
+        // touched list needs the counts in ascending expert order
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX) {
+                p.counts[e] = loc[i];
+                p.offsets[e] = run;
+                s_off[e] = run;
+            }
+            run += loc[i];
+            ntouched_before += (e < EX && loc[i] > 0) ? 1 : 0;
+        }
+        if (lane == kWave - 1) {
+            p.offsets[EX] = run;
+            s_off[EX] = run;
+        }
+        // touched experts, ascending: exclusive prefix of per-lane touched counts
+        int tincl = ntouched_before;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(tincl, s, kWave);
+            if (lane >= s) tincl += o;
+        }
+        int tpos = tincl - ntouched_before;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX) {
+                if (loc[i] > 0) p.touched[tpos++] = e;
+                else if (p.union_cnt) p.union_cnt[e] = 0;
+            }
+        }
+        if (lane == kWave - 1) {
+            p.hdr[0] = tincl;
+        }
+    }
+    __syncthreads();
+
+    // pass 2: stable scatter of the routed pairs
+    for (int base = a_begin; base < a_end; base += kWave) {
+        const int a = base + lane;
+        const bool valid = a < a_end;
+        const int e = valid ? p.ids[a] : 0;
+        const uint64_t peers = peers_of(e, valid);
+        const int leader = valid ? (__ffsll((long long)peers) - 1) : lane;
+        int old = 0;
+        if (valid && leader == lane) old = atomicAdd(&s_cnt[wv][e], __popcll(peers));
+        old = __shfl(old, leader, kWave);
+        if (valid) {
+            const int rank = __popcll(peers & lanemask_lt());
+            const int pos = s_off[e] + old + rank;
+            const int t = a / p.K, k = a - t * p.K;
+            p.pair_tok[pos] = t;
+            p.pair_slot[pos] = k;
+            p.pos[(size_t)t * p.slots + k] = pos;
+        }
+    }
+    // shared experts: pair A + s*T + t
+    for (int i = tid; i < p.S * p.T; i += blockDim.x) {
+        const int s = i / p.T, t = i - s * p.T;
+        const int pos = p.A + i;
+        p.pair_tok[pos] = t;
+        p.pair_slot[pos] = p.K + s;
+        p.pos[(size_t)t * p.slots + p.K + s] = pos;
+    }
+}
+
+hipError_t launch_group(const GroupParams &gp, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupWaves * kWave), 0, stream, gp);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,192 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/moe_sparse.h declares, and rejects invalid calls before any HIP call
+(so these run on a CPU-only host).  Pointers used here are never dereferenced:
+every call below fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from intra_expert_activation_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from intra_expert_activation_amd import _build
+        _build.build()
+    return moe.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "moe_sparse.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*\**\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) == 9, names
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(5):
+        s = moe.status_string(code)
+        assert s.startswith(("MOE_OK", "MOE_ERR_"))
+    assert moe.status_string(99) == "unknown moe_status"
+
+
+def _ws(shape, mode=moe.MOE_SPARSE):
+    n = ctypes.c_size_t()
+    rc = moe.lib().moe_workspace_size(ctypes.byref(shape), mode, ctypes.byref(n))
+    return rc, n.value
+
+
+GOOD = dict(T=8, H=2048, E=128, I=768, K=8, S=0, I_shared=0, dtype=moe.MOE_BF16, renormalize=1)
+
+
+def _shape(**kw):
+    d = dict(GOOD)
+    d.update(kw)
+    return moe.make_shape(**d)
+
+
+def test_workspace_size_valid_and_shape_only(L):
+    rc, n = _ws(_shape())
+    assert rc == moe.MOE_OK and n > 0 and n % 256 == 0
+    assert _ws(_shape())[1] == n                      # deterministic
+    assert _ws(_shape(T=64))[1] > n                   # grows with the batch
+    assert _ws(_shape(), moe.MOE_DENSE)[0] == moe.MOE_OK
+    assert _ws(_shape(T=0))[0] == moe.MOE_OK          # empty batch is valid
+    rc, n = _ws(_shape(H=256, E=8, I=512, K=2, dtype=moe.MOE_F32))
+    assert rc == moe.MOE_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(K=129), moe.MOE_ERR_INVALID_ARG),          # K > E
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(renormalize=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(S=1, I_shared=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(H=2000), moe.MOE_ERR_UNSUPPORTED),         # not 64 lanes x 16 bytes
+    (dict(H=1536), moe.MOE_ERR_UNSUPPORTED),         # 3 vectors per lane
+    (dict(I=770), moe.MOE_ERR_UNSUPPORTED),          # not a multiple of 32
+    (dict(I=32768), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=500, S=20, I_shared=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(K=33, E=128), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_workspace_size_rejects(L, kw, code):
+    assert _ws(_shape(**kw))[0] == code
+
+
+def test_invalid_mode(L):
+    assert _ws(_shape(), 5)[0] == moe.MOE_ERR_INVALID_ARG
+
+
+def _args(**ptrs):
+    a = moe.MoeFfnArgs()
+    base = dict(x=0x10000, router_logits=0x20000, w_gate=0x30000, w_up=0x40000, w_down=0x50000,
+                tau=0x60000, y=0x70000, workspace=0x80000)
+    base.update(ptrs)
+    for k, v in base.items():
+        setattr(a, k, v)
+    a.workspace_bytes = ptrs.get("workspace_bytes", 1 << 40)
+    return a
+
+
+def _ffn(shape, a, mode=moe.MOE_SPARSE):
+    return moe.lib().moe_sparse_expert_ffn(ctypes.byref(shape), mode, ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("missing", ["x", "router_logits", "w_gate", "w_up", "w_down", "y", "workspace"])
+def test_ffn_null_pointer(L, missing):
+    assert _ffn(_shape(), _args(**{missing: None})) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_ffn_tau_required_only_when_sparse(L):
+    assert _ffn(_shape(), _args(tau=None)) == moe.MOE_ERR_INVALID_ARG
+    # dense ignores tau: with a too-small workspace the call stops at that check
+    a = _args(tau=None)
+    a.workspace_bytes = 16
+    assert _ffn(_shape(), a, moe.MOE_DENSE) == moe.MOE_ERR_WORKSPACE
+
+
+def test_ffn_shared_pointers_required(L):
+    assert _ffn(_shape(S=2, I_shared=768), _args()) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [("x", 0x10008), ("w_gate", 0x30004), ("y", 0x70002),
+                                         ("router_logits", 0x20002), ("workspace", 0x80080)])
+def test_ffn_misaligned(L, field, value):
+    assert _ffn(_shape(), _args(**{field: value})) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_ffn_workspace_too_small(L):
+    need = _ws(_shape())[1]
+    a = _args()
+    a.workspace_bytes = need - 1
+    assert _ffn(_shape(), a) == moe.MOE_ERR_WORKSPACE
+
+
+def test_ffn_empty_batch_is_a_noop(L):
+    # T = 0: valid, nothing is enqueued (so no device is needed)
+    assert _ffn(_shape(T=0), _args(x=None, y=None)) == moe.MOE_OK
+
+
+def test_ffn_null_shape_or_args(L):
+    assert moe.lib().moe_sparse_expert_ffn(None, 0, ctypes.byref(_args()), None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_sparse_expert_ffn(ctypes.byref(_shape()), 0, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_route_validation(L):
+    f = moe.lib().moe_route_topk
+    assert f(0x1000, 4, 8, 9, 1, 0x2000, 0x3000, None) == moe.MOE_ERR_INVALID_ARG   # K > E
+    assert f(0x1000, 4, 8, 0, 1, 0x2000, 0x3000, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(0x1000, 4, 8, 2, 3, 0x2000, 0x3000, None) == moe.MOE_ERR_INVALID_ARG   # renormalize
+    assert f(None, 4, 8, 2, 1, 0x2000, 0x3000, None) == moe.MOE_ERR_INVALID_ARG
+    assert f(0x1002, 4, 8, 2, 1, 0x2000, 0x3000, None) == moe.MOE_ERR_INVALID_ARG   # misaligned
+    assert f(0x1000, 4, 600, 2, 1, 0x2000, 0x3000, None) == moe.MOE_ERR_UNSUPPORTED  # E > 512
+    assert f(None, 0, 8, 2, 1, None, None, None) == moe.MOE_OK                        # empty batch
+
+
+def _cal(shape, q, Tc=64, per_expert=0, ws_bytes=1 << 40, **ptr):
+    p = dict(x=0x10000, logits=0x20000, wg=0x30000, wsg=0x40000, tau=0x50000, ws=0x60000)
+    p.update(ptr)
+    return moe.lib().moe_calibrate_threshold(ctypes.byref(shape), p["x"], p["logits"], Tc, p["wg"],
+                                             p["wsg"], ctypes.c_float(q), per_expert, p["tau"],
+                                             p["ws"], ws_bytes, None)
+
+
+def test_calibrate_validation(L):
+    s = _shape()
+    for q in (-0.1, 1.5, float("nan")):
+        assert _cal(s, q) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(s, 0.5, Tc=0) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(s, 0.5, per_expert=2) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(s, 0.5, tau=None) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(_shape(S=1, I_shared=768), 0.5, wsg=None) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(s, 0.5, x=0x10004) == moe.MOE_ERR_INVALID_ARG
+    assert _cal(s, 0.5, ws_bytes=10) == moe.MOE_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert moe.lib().moe_calibrate_workspace_size(ctypes.byref(s), 64, ctypes.byref(n)) == moe.MOE_OK
+    assert n.value > 0
+
+
+def test_timer_validation(L):
+    assert moe.lib().moe_timer_create(None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_timer_destroy(None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_timer_elapsed_ms(None, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        moe.lib()

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Bars (checked in parity_util.check_layer): routing ids exact, masks and
+per-expert unions bit-exact outside the +-1e-3*tau band, layer output within
+relative L2 2e-3 for bf16 weights (fp32 accumulation) and 1e-5 for the fp32
+layer.  The thresholds fed to both sides are the oracle's own calibration.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from intra_expert_activation_amd import moe, synth
+
+from parity_util import cached_layer, check_layer, gpu_ffn, layer_to_device, rel_l2, unpack_bits
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-3
+TOL_F32 = 1e-5
+
+
+def _tau(L, c, q, calib_tokens=None, per_expert=False):
+    xc, lc = synth.make_tokens(c, 1)
+    if calib_tokens:
+        xc, lc = xc[:calib_tokens], lc[:calib_tokens]
+    return oracle.calibrate(L, xc, lc, q, per_expert=per_expert)
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 layer (H 256, E 8, I 512, top-2, 16 tokens, tau at the 80% quantile)
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_sparse_and_dense():
+    c, L = cached_layer(1)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2)
+    tau = _tau(L, c, 0.80)
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_F32)
+    assert 0.05 < s["active"] < 0.5
+    check_layer(L, DL, x, logits, None, mode=moe.MOE_DENSE, tol=TOL_F32)
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_tau_zero_is_dense_bitwise(cfg):
+    c, L = cached_layer(cfg, (("E", 16), ("I", 256)) if cfg == 4 else ())
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2)
+    x, logits = x[:13], logits[:13]
+    sp = gpu_ffn(DL, x, logits, 0.0)
+    de = gpu_ffn(DL, x, logits, None, mode=moe.MOE_DENSE)
+    assert np.array_equal(sp["y"], de["y"])
+    Imax = max(L["I"], L["I_shared"])
+    m = unpack_bits(sp["mask_bits"], Imax)
+    assert m[:, :L["K"], :L["I"]].all() and not m[:, :L["K"], L["I"]:].any()
+    assert m[:, L["K"]:, :L["I_shared"]].all()
+    rows = np.where(np.arange(L["E"] + L["S"]) < L["E"], L["I"], L["I_shared"])
+    touched = np.isin(np.arange(L["E"] + L["S"]), np.r_[sp["topk_ids"].ravel(), L["E"] + np.arange(L["S"])])
+    np.testing.assert_array_equal(sp["union_cnt"], np.where(touched, rows, 0))
+
+
+def test_tau_infinite_gives_zero():
+    c, L = cached_layer(4, (("E", 16), ("I", 256)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2)
+    g = gpu_ffn(DL, x[:9], logits[:9], np.inf)
+    assert (g["y"] == 0).all() and (g["mask_bits"] == 0).all() and (g["union_cnt"] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Qwen-MoE-style decode layer (H 2048, E 128, I 768, top-8, q = 0.85)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_qwen_decode(T):
+    c, L = cached_layer(2)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, 0.85)
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+    print(f"T={T} err={s['err']:.2e} band={s['band']} flips={s['flips']} active={s['active']:.3f}")
+    assert 0.05 < s["active"] < 0.3
+
+
+def test_qwen_decode_dense():
+    c, L = cached_layer(2)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 8)
+    check_layer(L, DL, x, logits, None, mode=moe.MOE_DENSE, tol=TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# DeepSeek-V2-Lite-style layer: 64 routed (top-6, no renormalisation) + 2
+# shared experts on the sparse path, Zipf-skewed routing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,q", [(1, 0.85), (8, 0.85), (32, 0.85), (64, 0.85), (64, 0.70)])
+def test_deepseek_shared(T, q):
+    c, L = cached_layer(4)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, q)
+    assert tau[-1] != tau[0]  # the shared experts have their own threshold
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+    print(f"T={T} q={q} err={s['err']:.2e} band={s['band']} flips={s['flips']}")
+
+
+def test_deepseek_per_expert_tau():
+    c, L = cached_layer(4)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 32)
+    tau = _tau(L, c, 0.85, per_expert=True)
+    check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+
+
+# ---------------------------------------------------------------------------
+# Mixtral-style layer (H 4096, E 8, I 14336, top-2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,q", [(16, 0.9), (40, 0.7)])
+def test_mixtral_reduced_ragged(T, q):
+    # full H and E with I cut to 1056 (33 words: ragged row chunks) so the
+    # oracle checks every token
+    c, L = cached_layer(3, (("I", 1056),))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, q)
+    check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_mixtral_full_sampled(T):
+    c, L = cached_layer(3)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, 0.9, calib_tokens=8)
+    rows = np.unique(np.r_[0, T - 1, T // 2])
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16, rows_idx=rows)
+    print(f"T={T} err={s['err']:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Qwen-MoE-style prefill (4096 tokens): every output row the oracle checks is
+# sampled; unions are checked against the GPU's own masks at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("q", [0.5, 0.9])
+def test_qwen_prefill_sampled(q):
+    c, L = cached_layer(5)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2)
+    tau = _tau(L, c, q, calib_tokens=16)
+    rows = np.random.default_rng(7).choice(x.shape[0], 6, replace=False)
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16, rows_idx=np.sort(rows))
+    print(f"q={q} err={s['err']:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("over,T", [
+    ((("E", 4), ("K", 4)), 5),                                      # K = E
+    ((("E", 300), ("K", 3), ("I", 64)), 50),                        # many experts
+    ((("H", 512), ("E", 6), ("I", 96)), 7),                         # H = 512 (one vector per lane)
+    ((("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 3),              # H = 8192 (16 vectors per lane)
+])
+def test_edge_shapes_bf16(over, T):
+    c, L = cached_layer(2, over)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, 0.85, calib_tokens=8)
+    check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+
+
+def test_shared_wider_than_routed():
+    c, L = cached_layer(4, (("E", 12), ("I", 128), ("I_shared", 320), ("S", 1)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 11)
+    tau = _tau(L, c, 0.7, calib_tokens=8)
+    check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+
+
+def test_fp32_two_vectors_per_lane():
+    c, L = cached_layer(1, (("H", 512), ("I", 160), ("E", 5)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 16)
+    tau = _tau(L, c, 0.6)
+    check_layer(L, DL, x, logits, tau, tol=TOL_F32)
+
+
+def test_empty_batch():
+    c, L = cached_layer(1)
+    DL = layer_to_device(L)
+    x = torch.empty((0, L["H"]), dtype=torch.float32, device="cuda")
+    lg = torch.empty((0, L["E"]), dtype=torch.float32, device="cuda")
+    out = moe.sparse_expert_ffn(x, lg, DL["w_gate"], DL["w_up"], DL["w_down"],
+                                torch.zeros(L["E"], device="cuda"), K=L["K"], want_masks=False)
+    torch.cuda.synchronize()
+    assert out["y"].shape == (0, L["H"])
+
+
+def test_nan_input_is_active_and_propagates():
+    c, L = cached_layer(1)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2)
+    x = x.copy()
+    x[3, 17] = np.nan
+    tau = _tau(L, c, 0.8)
+    g = gpu_ffn(DL, x, logits, tau)
+    assert np.isnan(g["y"][3]).all()
+    assert np.isfinite(np.delete(g["y"], 3, axis=0)).all()
+    assert unpack_bits(g["mask_bits"][3], L["I"]).all()
+
+
+def test_deterministic():
+    c, L = cached_layer(4)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 64)
+    tau = _tau(L, c, 0.85, calib_tokens=16)
+    a = gpu_ffn(DL, x, logits, tau)
+    b = gpu_ffn(DL, x, logits, tau)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------
+# Routing alone
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,K,renorm", [(1, 8, 2, 1), (64, 128, 8, 1), (33, 64, 6, 0), (4096, 128, 8, 1),
+                                          (7, 512, 32, 1), (5, 3, 3, 0)])
+def test_route_topk(T, E, K, renorm):
+    rng = np.random.default_rng([T, E, K])
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[: T // 2, 1] = logits[: T // 2, 0]  # ties: the lower id first
+    ids, w = moe.route_topk(torch.from_numpy(logits).cuda(), K, bool(renorm))
+    torch.cuda.synchronize()
+    oids, ow = oracle.route(logits, K, renorm)
+    np.testing.assert_array_equal(ids.cpu().numpy(), oids)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=2e-6, atol=1e-8)
+
+
+# ---------------------------------------------------------------------------
+# Calibration on the GPU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,q,per_expert", [(1, 0.8, False), (2, 0.85, False), (4, 0.85, False),
+                                              (4, 0.7, True), (1, 0.0, False), (1, 1.0, False)])
+def test_calibrate(cfg, q, per_expert):
+    c, L = cached_layer(cfg)
+    DL = layer_to_device(L)
+    xc, lc = synth.make_tokens(c, 1)
+    dt = L["dtype"]
+    from parity_util import dev_tensor
+    tau_g = moe.calibrate_threshold(dev_tensor(xc, dt), torch.from_numpy(lc).cuda(), DL["w_gate"], q,
+                                    K=L["K"], shared_gate=DL.get("ws_gate"), per_expert=per_expert)
+    torch.cuda.synchronize()
+    tau_g = tau_g.cpu().numpy().astype(np.float64)
+    tau_o = oracle.calibrate(L, xc, lc, q, per_expert=per_expert)
+    # the order statistic moves by at most the largest score error (fp32 vs fp64)
+    finite = np.isfinite(tau_o)
+    np.testing.assert_array_equal(np.isfinite(tau_g), finite)
+    np.testing.assert_allclose(tau_g[finite], tau_o[finite], rtol=1e-4, atol=2e-6)
+    if q in (0.0, 1.0):
+        return
+    # exact count: the FFN's masks on the calibration tokens use the same fp32
+    # scores, so floor(q*N) routed scores fall strictly below tau (ties aside)
+    g = gpu_ffn(DL, xc, lc, tau_g.astype(np.float32))
+    if per_expert:
+        return
+    m = unpack_bits(g["mask_bits"], max(L["I"], L["I_shared"]))
+    routed_inactive = (~m[:, :L["K"], :L["I"]]).sum()
+    N = xc.shape[0] * L["K"] * L["I"]
+    kappa = int(np.floor(float(np.float32(q)) * N))
+    assert kappa - 3 <= routed_inactive <= kappa, (routed_inactive, kappa)
+    if L["S"]:
+        sh_inactive = (~m[:, L["K"]:, :L["I_shared"]]).sum()
+        Ns = xc.shape[0] * L["S"] * L["I_shared"]
+        ks = int(np.floor(float(np.float32(q)) * Ns))
+        assert ks - 3 <= sh_inactive <= ks
