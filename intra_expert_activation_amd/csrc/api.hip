@@ -59,17 +59,17 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
 
     // rows per projection workgroup: the smallest multiple of 32 that keeps the
     // grid at or below ~2048 workgroups (8 per CU on 256 CUs)
+    // the projection kernel gives each workgroup one 32-row mask word
     p->R = 32;
-    while (p->R < kMaxRowsPerChunk &&
-           (long long)p->max_touched * ((p->Imax + p->R - 1) / p->R) > 2048)
-        p->R += 32;
-    p->C = (p->Imax + p->R - 1) / p->R;
+    p->C = p->Imax / 32;
 
-    // token tile: covers the mean pairs per touched routed expert, bounded by
-    // the registers the hidden-state tile takes (TT * NS vectors <= 32)
+    // token tile: covers the mean pairs per touched routed expert; at most 8
+    // (the dot products of larger tiles outrun the weight stream), and at most
+    // 16 vectors of hidden states per lane (a wavefront holds NS/4 of a row)
     const int touched_routed = p->A < p->E ? p->A : p->E;
     const int mean_ne = touched_routed > 0 ? (p->A + touched_routed - 1) / touched_routed : 1;
-    const int tt_cap = p->NS <= 4 ? 8 : (p->NS == 8 ? 4 : 2);
+    const int nsw = p->NS <= 4 ? 1 : p->NS / 4;
+    const int tt_cap = 16 / nsw < 8 ? 16 / nsw : 8;
     p->TT = 1;
     while (p->TT < mean_ne && p->TT < tt_cap) p->TT *= 2;
 

@@ -19,15 +19,52 @@
 
 namespace moe {
 
+template <class Tr, int UR, int TB>
+struct DownBatch {
+    typename Tr::V w[UR];
+    float h[UR][TB];
+};
+
+// Loads of the wavefront's next UR rows of the split: this lane's 16-byte
+// vector of each down row and the tile's h values of each row.
+template <class Tr, int UR, int TB, int MODE>
+__device__ __forceinline__ void load_down_batch(DownBatch<Tr, UR, TB> &bt, const typename Tr::V *Wd,
+                                                const float *hb, const uint16_t *list, int i0, int hi,
+                                                int n, int t0, int nt, int rowV)
+{
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+        const int i = i0 + 4 * u;
+        const int j = (i < hi) ? ((MODE == MOE_DENSE) ? i : (int)list[i]) : -1;
+        bt.w[u] = (j >= 0) ? Wd[(size_t)j * rowV] : Tr::zero();
+#pragma unroll
+        for (int t = 0; t < TB; ++t) bt.h[u][t] = (j >= 0 && t < nt) ? hb[(size_t)j * n + t0 + t] : 0.f;
+    }
+}
+
+template <class Tr, int UR, int TB>
+__device__ __forceinline__ void fma_down_batch(const DownBatch<Tr, UR, TB> &bt, float (&acc)[TB][Tr::kEpl])
+{
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+        float wf[Tr::kEpl];
+        Tr::unpack(bt.w[u], wf);
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < Tr::kEpl; ++e) acc[t][e] = fmaf(bt.h[u][t], wf[e], acc[t][e]);
+    }
+}
+
 template <class Tr, int TB, int MODE>
 __global__ __launch_bounds__(256) void k_down(DownParams p)
 {
     using V = typename Tr::V;
     constexpr int EPL = Tr::kEpl;
-    constexpr int UR = 4;  // rows in flight per wavefront
-    __shared__ uint16_t s_list[kMaxRows];
-    __shared__ int s_wpre[kMaxRows / 32 + 1];
-    __shared__ float s_red[3][TB][kWave * EPL];
+    constexpr int UR = 4;  // rows per batch per wavefront; two batches in flight
+    extern __shared__ uint16_t s_list[];  // the expert's union rows, ascending
+    __shared__ float s_red[2][TB][kWave * EPL];
+    __shared__ int s_wpre[4];
 
     const int per_e = p.NCT * p.NSPLIT;
     const int s = blockIdx.x / per_e;
@@ -41,11 +78,12 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
     const int n = p.counts[xe];
     const int off = p.offsets[xe];
     const int rowV = p.NCT * kWave;
-    const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
-    const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat;
-    const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int cv = ct * kWave + lane;  // this lane's vector of each row
+    const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
+    const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat + cv;
+    const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
 
     // ---- union row list -----------------------------------------------------
     int U;
@@ -60,7 +98,6 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
         int cnt = 0;
         for (int i = 0; i < per; ++i)
             if (w_begin + i < nw) cnt += __popc(uw[w_begin + i]);
-        // block exclusive scan of cnt (256 threads, 4 wavefronts)
         int incl = cnt;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
@@ -94,7 +131,8 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
 
     const int lo = (int)(((long long)U * sp) / p.NSPLIT);
     const int hi = (int)(((long long)U * (sp + 1)) / p.NSPLIT);
-    const int cv = ct * kWave + lane;  // this lane's vector of each row
+    const int mine = hi - lo - wave > 0 ? (hi - lo - wave + 3) / 4 : 0;  // rows of this wavefront
+    const int nb = (mine + UR - 1) / UR;
 
     for (int t0 = 0; t0 < n; t0 += TB) {
         const int nt = min(TB, n - t0);
@@ -104,36 +142,40 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
 
-        for (int ib = lo + wave; ib < hi; ib += 4 * UR) {
-            V wv[UR];
-            float hv[UR][TB];
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int i = ib + 4 * u;
-                const int j = (i < hi) ? ((MODE == MOE_DENSE) ? i : (int)s_list[i]) : -1;
-                wv[u] = (j >= 0) ? Wd[(size_t)j * rowV + cv] : Tr::zero();
-#pragma unroll
-                for (int t = 0; t < TB; ++t)
-                    hv[u][t] = (j >= 0 && t < nt) ? hb[(size_t)j * n + t0 + t] : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                float wf[EPL];
-                Tr::unpack(wv[u], wf);
-#pragma unroll
-                for (int t = 0; t < TB; ++t)
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[t][e] = fmaf(hv[u][t], wf[e], acc[t][e]);
-            }
+        // rows lo + wave + 4 i of the split, batches of UR, two in flight
+        DownBatch<Tr, UR, TB> A, B;
+        if (nb > 0) load_down_batch<Tr, UR, TB, MODE>(A, Wd, hb, s_list, lo + wave, hi, n, t0, nt, rowV);
+#pragma unroll 1
+        for (int b = 0; b < nb; b += 2) {
+            if (b + 1 < nb)
+                load_down_batch<Tr, UR, TB, MODE>(B, Wd, hb, s_list, lo + wave + 4 * UR * (b + 1), hi, n, t0, nt, rowV);
+            fma_down_batch<Tr, UR, TB>(A, acc);
+            if (b + 1 >= nb) break;
+            if (b + 2 < nb)
+                load_down_batch<Tr, UR, TB, MODE>(A, Wd, hb, s_list, lo + wave + 4 * UR * (b + 2), hi, n, t0, nt, rowV);
+            fma_down_batch<Tr, UR, TB>(B, acc);
         }
 
-        // sum the 4 wavefronts in a fixed order: wave 0 + (1 + (2 + 3))... via LDS
-        __syncthreads();
-        if (wave > 0) {
+        // wavefront sums in a fixed order: (w0 + w2) + (w1 + w3)
+        if (wave >= 2) {
 #pragma unroll
             for (int t = 0; t < TB; ++t)
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) s_red[wave - 1][t][lane * EPL + e] = acc[t][e];
+                for (int e = 0; e < EPL; ++e) s_red[wave - 2][t][lane * EPL + e] = acc[t][e];
+        }
+        __syncthreads();
+        if (wave < 2) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[t][e] += s_red[wave][t][lane * EPL + e];
+        }
+        __syncthreads();
+        if (wave == 1) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) s_red[0][t][lane * EPL + e] = acc[t][e];
         }
         __syncthreads();
         if (wave == 0) {
@@ -142,15 +184,14 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
                 if (t >= nt) break;
                 float o[EPL];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    o[e] = acc[t][e] + s_red[0][t][lane * EPL + e] + s_red[1][t][lane * EPL + e] +
-                           s_red[2][t][lane * EPL + e];
+                for (int e = 0; e < EPL; ++e) o[e] = acc[t][e] + s_red[0][t][lane * EPL + e];
                 float *dst = p.partial + ((size_t)sp * p.P + off + t0 + t) * p.H + (size_t)cv * EPL;
 #pragma unroll
                 for (int e = 0; e < EPL; e += 4)
                     *reinterpret_cast<float4 *>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
             }
         }
+        __syncthreads();  // s_red is rewritten by the next tile
     }
 }
 
@@ -158,8 +199,9 @@ template <class Tr, int TB>
 static hipError_t launch_down_t(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
 {
     const dim3 grid(pl.max_touched * pl.NCT * pl.NSPLIT), block(256);
+    const size_t lds = (size_t)pl.Imax * sizeof(uint16_t);
     if (mode == MOE_DENSE) hipLaunchKernelGGL((k_down<Tr, TB, MOE_DENSE>), grid, block, 0, st, dp);
-    else hipLaunchKernelGGL((k_down<Tr, TB, MOE_SPARSE>), grid, block, 0, st, dp);
+    else hipLaunchKernelGGL((k_down<Tr, TB, MOE_SPARSE>), grid, block, lds, st, dp);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Expert projection: dense gate GEMV, SiLU score, threshold mask, wavefront
-// ballot of the active neurons, and the up projection of the active rows only.
+// Expert projection: dense gate GEMV, SiLU score, threshold mask, ballot of
+// the active neurons, and the up projection of the active rows only.
 //
 // gist.science page of arXiv 2605.08575, Technical Summary, Methodology:
 //   Gate Projection    every gate row of a selected expert is read (dense);
@@ -7,218 +7,243 @@
 //   Fused Up-Down      only active neurons' up rows are fetched.
 // The down projection of the active rows is the next kernel (down.hip).
 //
-// Work decomposition.  One workgroup (4 wavefronts) owns R consecutive neuron
-// rows of one touched expert and loops over that expert's tokens in register
-// tiles of TT tokens.  A lane owns a fixed set of columns of every row
-// (NS 16-byte vectors, 64 lanes interleaved), so its slice of each token's
-// hidden state is loaded once per tile and kept in registers while rows
-// stream through.  Row dot products are finished with a wavefront reduction.
-//   phase G  all R gate rows: g, a = SiLU(g), m = NOT(|a| < tau); a goes to LDS,
-//            m to LDS bit words (the mask), their OR over the tile's tokens to
-//            the tile's active-row words;
-//   phase U  the active rows only: u = x . w_up, h = m ? a*u : 0.
-// h is written to a per-expert block [rows][n_e] (n_e = the expert's pairs);
-// rows inactive for the whole tile get h = 0 without touching w_up.  Every
-// workgroup owns whole 32-bit mask words (R is a multiple of 32), so masks and
-// the per-expert union are written without atomics.
+// Work decomposition (gfx950).  A workgroup owns 32 consecutive neuron rows of
+// one touched expert -- one 32-bit mask word -- and every token of that
+// expert, in tiles of TT tokens.  Its NW wavefronts split each row's columns
+// (K-split): wavefront w reads the w-th 1/NW of every row (NSW 16-byte vectors
+// per lane, contiguous 1 KB blocks), so it keeps only its slice of the token
+// tile's hidden states in registers.  Rows stream in batches of UR with the
+// next batch's loads issued before the current batch is reduced (software
+// pipelining), and the UR x TT partial dot products of a batch are summed
+// across the 64 lanes by one transposed reduction (wave_reduce.h).  The NW
+// partials of each (row, token) meet in LDS and are added in a fixed order.
+//   gate  all 32 rows -> g, a = SiLU(g), m = NOT(|a| < tau), mask word per
+//         token, active-row word (OR over the tile's tokens);
+//   up    the active rows only -> u, h = m ? a*u : 0 (a select: an inactive
+//         neuron contributes exactly 0).
+// h goes to a per-expert block [rows][n_e]; rows inactive for every token of
+// the tile get h = 0 without reading w_up.  Mask words and the per-expert
+// union word are written whole, without atomics in global memory.
 #include "moe_internal.h"
+#include "wave_reduce.h"
 
 namespace moe {
 
-template <class Tr, int NS, int TT, int MODE>
-__global__ __launch_bounds__(256) void k_proj(ProjParams p)
+constexpr int kChunk = 32;  // rows per workgroup = bits per mask word
+
+// Issue the loads of UR consecutive rows starting at row r (this lane's NSW
+// vectors of each).
+template <class Tr, int UR, int NSW>
+__device__ __forceinline__ void load_rows(typename Tr::V (&buf)[UR][NSW], const typename Tr::V *W, int r,
+                                          int rowV)
+{
+#pragma unroll
+    for (int u = 0; u < UR; ++u)
+#pragma unroll
+        for (int k = 0; k < NSW; ++k) buf[u][k] = W[(size_t)(r + u) * rowV + k * kWave];
+}
+
+// Issue the loads of the next UR rows whose bits are set in `rest` (ascending),
+// clearing those bits; missing rows load nothing and read as zero.
+template <class Tr, int UR, int NSW>
+__device__ __forceinline__ void load_active_rows(typename Tr::V (&buf)[UR][NSW], const typename Tr::V *W,
+                                                 uint32_t &rest, int rowV)
+{
+#pragma unroll
+    for (int u = 0; u < UR; ++u) {
+        const int r = rest ? __ffs(rest) - 1 : -1;
+        rest &= rest - 1;
+#pragma unroll
+        for (int k = 0; k < NSW; ++k) buf[u][k] = (r >= 0) ? W[(size_t)r * rowV + k * kWave] : Tr::zero();
+    }
+}
+
+// Partial dot products of UR rows with the TT tokens over this wavefront's
+// columns, summed across the lanes by one transposed reduction; the lane that
+// owns value (u, t) stores it at s_part[wave][slot0 + u][t].
+template <class Tr, int UR, int NSW, int TT, int NW>
+__device__ __forceinline__ void reduce_batch(const typename Tr::V (&buf)[UR][NSW],
+                                             const typename Tr::V (&xr)[TT][NSW],
+                                             float (&s_part)[NW][kChunk][TT], int wave, int slot0, int lane,
+                                             int kidx, bool owner)
+{
+    constexpr int M = UR * TT;
+    float v[M];
+#pragma unroll
+    for (int u = 0; u < UR; ++u)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < NSW; ++k) acc = Tr::dot(buf[u][k], xr[t][k], acc);
+            v[u * TT + t] = acc;
+        }
+    const float part = xreduce<M>(v, lane);
+    if (owner) s_part[wave][slot0 + kidx / TT][kidx % TT] = part;
+}
+
+template <class Tr, int NW, int NSW, int TT, int MODE>
+__global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
 {
     using V = typename Tr::V;
-    constexpr int UR = (16 / NS) > 8 ? 8 : ((16 / NS) < 1 ? 1 : (16 / NS));  // rows in flight per wavefront
-    constexpr int kWords = kMaxRowsPerChunk / 32;
+    // rows per batch: at most 32 partial sums per reduction and 4 vectors of
+    // weights per lane per batch (two batches are in flight)
+    constexpr int UR_T = 32 / TT < 1 ? 1 : 32 / TT;
+    constexpr int UR_V = 4 / NSW < 1 ? 1 : 4 / NSW;
+    constexpr int UR = UR_T < UR_V ? UR_T : UR_V;
+    constexpr int M = UR * TT;        // values per reduction
+    constexpr int NB = kChunk / UR;   // batches per 32 rows (even)
+    static_assert(NB % 2 == 0, "ping-pong needs an even batch count");
 
-    __shared__ float s_a[TT][kMaxRowsPerChunk];
-    __shared__ uint32_t s_mask[TT][kWords];
-    __shared__ uint32_t s_act[kWords];
-    __shared__ uint32_t s_union[kWords];
-    __shared__ int s_list[kMaxRowsPerChunk];
-    __shared__ int s_nact;
+    __shared__ float s_part[NW][kChunk][TT];  // per-wavefront partial dots
+    __shared__ float s_a[kChunk][TT];         // scores of the tile
+    __shared__ uint32_t s_mask[TT];           // mask word per token of the tile
+    __shared__ uint32_t s_act;                // rows active for some token of the tile
 
-    const int s = blockIdx.x / p.C;
-    const int c = blockIdx.x - s * p.C;
+    const int nw_per_e = p.C;
+    const int s = blockIdx.x / nw_per_e;
+    const int c = blockIdx.x - s * nw_per_e;
     if (s >= p.hdr[0]) return;
     const int xe = p.touched[s];
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
-    const int r0 = c * p.R;
+    const int r0 = c * kChunk;
     if (r0 >= Ie) return;
-    const int nr = min(p.R, Ie - r0);  // multiple of 32
     const int n = p.counts[xe];
     const int off = p.offsets[xe];
-    const int rowV = NS * kWave;       // 16-byte vectors per row (= H / epl)
+    constexpr int rowV = NW * NSW * kWave;  // 16-byte vectors per row (H / epl)
     const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
-    const V *Wg = reinterpret_cast<const V *>(shared ? p.swg : p.wg) + mat;
-    const V *Wu = reinterpret_cast<const V *>(shared ? p.swu : p.wu) + mat;
-    const V *X = reinterpret_cast<const V *>(p.x);
-    float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
-    const float tau = (MODE == MOE_SPARSE) ? p.tau[xe] : 0.f;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwords = nr / 32;
-
-    if (threadIdx.x < kWords) s_union[threadIdx.x] = 0u;
+    const int vbase = wave * NSW * kWave + lane;  // this lane's first vector of a row
+    const V *Wg = reinterpret_cast<const V *>(shared ? p.swg : p.wg) + mat + (size_t)r0 * rowV + vbase;
+    const V *Wu = reinterpret_cast<const V *>(shared ? p.swu : p.wu) + mat + (size_t)r0 * rowV + vbase;
+    const V *X = reinterpret_cast<const V *>(p.x) + vbase;
+    float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie)
+                + (size_t)r0 * n;
+    const float tau = (MODE == MOE_SPARSE) ? p.tau[xe] : 0.f;
+    const int kidx = xreduce_index<M>(lane);
+    const bool owner = xreduce_owner<M>(lane);
+    uint32_t uni = 0;  // union word of this chunk (thread 0)
 
     for (int t0 = 0; t0 < n; t0 += TT) {
         const int nt = min(TT, n - t0);
-        __syncthreads();  // LDS of the previous tile is no longer read
-        if (threadIdx.x < TT * kWords) (&s_mask[0][0])[threadIdx.x] = 0u;
-        if (threadIdx.x < kWords) s_act[threadIdx.x] = 0u;
-
-        // this lane's columns of the tile's hidden states
-        V xr[TT][NS];
+        // this wavefront's slice of the tile's hidden states
+        V xr[TT][NSW];
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             const int tok = (t < nt) ? p.pair_tok[off + t0 + t] : -1;
 #pragma unroll
-            for (int v = 0; v < NS; ++v)
-                xr[t][v] = (tok >= 0) ? X[(size_t)tok * rowV + v * kWave + lane] : Tr::zero();
+            for (int k = 0; k < NSW; ++k)
+                xr[t][k] = (tok >= 0) ? X[(size_t)tok * rowV + k * kWave] : Tr::zero();
+        }
+        if (threadIdx.x < TT) s_mask[threadIdx.x] = 0u;
+        if (threadIdx.x == 0) s_act = 0u;
+
+        // ---- gate: 32 rows in NB batches, two in flight (ping-pong) ---------
+        {
+            V bufA[UR][NSW], bufB[UR][NSW];
+            load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);
+#pragma unroll 1
+            for (int b = 0; b < NB; b += 2) {
+                load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+                reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+                if (b + 2 < NB) load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+                reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+            }
         }
         __syncthreads();
 
-        // ---- phase G: gate rows r = wave + 4 i -------------------------------
-        for (int rb = wave; rb < nr; rb += 4 * UR) {
-            V wv[UR][NS];
+        // ---- scores, masks, active rows -------------------------------------
+        for (int i = threadIdx.x; i < kChunk * TT; i += NW * kWave) {
+            const int r = i / TT, t = i - r * TT;
+            float g = 0.f;
 #pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int r = rb + 4 * u;
-#pragma unroll
-                for (int v = 0; v < NS; ++v)
-                    wv[u][v] = (r < nr) ? Wg[(size_t)(r0 + r) * rowV + v * kWave + lane] : Tr::zero();
-            }
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int r = rb + 4 * u;
-                if (r >= nr) break;
-                float g[TT];
-#pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int v = 0; v < NS; ++v) acc = Tr::dot(wv[u][v], xr[t][v], acc);
-                    g[t] = wave_sum(acc);
-                }
-                if (MODE == kModeScore) {
-#pragma unroll
-                    for (int t = 0; t < TT; ++t)
-                        if (lane == t && t < nt) hb[(size_t)(r0 + r) * n + t0 + t] = fabsf(silu(g[t]));
-                } else {
-                    uint32_t mb = 0;
-#pragma unroll
-                    for (int t = 0; t < TT; ++t) {
-                        const float a = silu(g[t]);
-                        const bool m = (t < nt) && (MODE == MOE_DENSE || !(fabsf(a) < tau));
-                        mb |= (m ? 1u : 0u) << t;
-                        if (lane == t) s_a[t][r] = a;
-                    }
-                    if (lane < TT && ((mb >> lane) & 1u)) atomicOr(&s_mask[lane][r >> 5], 1u << (r & 31));
-                    if (lane == 0 && mb) atomicOr(&s_act[r >> 5], 1u << (r & 31));
+            for (int w = 0; w < NW; ++w) g += s_part[w][r][t];
+            const float a = silu(g);
+            if (MODE == kModeScore) {
+                if (t < nt) hb[(size_t)r * n + t0 + t] = fabsf(a);
+            } else {
+                s_a[r][t] = a;
+                const bool m = (t < nt) && (MODE == MOE_DENSE || !(fabsf(a) < tau));
+                if (m) {
+                    atomicOr(&s_mask[t], 1u << r);
+                    atomicOr(&s_act, 1u << r);
                 }
             }
         }
-        if (MODE == kModeScore) continue;
+        if (MODE == kModeScore) {
+            __syncthreads();  // s_part is rewritten by the next tile
+            continue;
+        }
+        __syncthreads();
+        const uint32_t act = __builtin_amdgcn_readfirstlane(s_act);
+        const int nact = __popc(act);
+
+        // ---- up: active rows only, in ascending order ----------------------
+        if (nact > 0) {
+            const int nbu = (nact + UR - 1) / UR;
+            uint32_t rest = act;  // rows not yet issued (scalar)
+            V bufA[UR][NSW], bufB[UR][NSW];
+            load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+#pragma unroll 1
+            for (int b = 0; b < nbu; b += 2) {
+                if (b + 1 < nbu) load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, rowV);
+                reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+                if (b + 1 >= nbu) break;
+                if (b + 2 < nbu) load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+                reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+            }
+        }
         __syncthreads();
 
-        // ---- compact the tile's active rows (ascending) ----------------------
-        if (wave == 0) {
-            int base = 0;
-            for (int r = lane; r < ((nr + kWave - 1) / kWave) * kWave; r += kWave) {
-                const bool act = (r < nr) && ((s_act[r >> 5] >> (r & 31)) & 1u);
-                const uint64_t b = __ballot(act);
-                if (act) s_list[base + __popcll(b & lanemask_lt())] = r;
-                base += __popcll(b);
-            }
-            if (lane == 0) s_nact = base;
-        }
-        // rows inactive for every token of the tile: h = 0, w_up not read
-        for (int i = threadIdx.x; i < nr * nt; i += blockDim.x) {
+        // ---- h for every row of the tile, masks, union ------------------------
+        for (int i = threadIdx.x; i < kChunk * nt; i += NW * kWave) {
             const int r = i / nt, t = i - r * nt;
-            if (!((s_act[r >> 5] >> (r & 31)) & 1u)) hb[(size_t)(r0 + r) * n + t0 + t] = 0.f;
+            float hv = 0.f;
+            if ((act >> r) & 1u) {
+                const int slot = __popc(act & ((1u << r) - 1u));  // rank among active rows
+                float u = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) u += s_part[w][slot][t];
+                const bool m = (s_mask[t] >> r) & 1u;
+                hv = m ? s_a[r][t] * u : 0.f;
+            }
+            hb[(size_t)r * n + t0 + t] = hv;
         }
-        __syncthreads();
-        const int nact = s_nact;
-
-        // ---- phase U: up rows of the active neurons only ---------------------
-        for (int ib = wave; ib < nact; ib += 4 * UR) {
-            V wv[UR][NS];
-            int rr[UR];
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int i = ib + 4 * u;
-                rr[u] = (i < nact) ? s_list[i] : -1;
-#pragma unroll
-                for (int v = 0; v < NS; ++v)
-                    wv[u][v] = (rr[u] >= 0) ? Wu[(size_t)(r0 + rr[u]) * rowV + v * kWave + lane] : Tr::zero();
-            }
-#pragma unroll
-            for (int u = 0; u < UR; ++u) {
-                const int r = rr[u];
-                if (r < 0) break;
-#pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    float acc = 0.f;
-#pragma unroll
-                    for (int v = 0; v < NS; ++v) acc = Tr::dot(wv[u][v], xr[t][v], acc);
-                    const float uu = wave_sum(acc);
-                    if (lane == t && t < nt) {
-                        const bool m = (s_mask[t][r >> 5] >> (r & 31)) & 1u;
-                        // a select, not a multiply: an inactive neuron contributes exactly 0
-                        hb[(size_t)(r0 + r) * n + t0 + t] = m ? s_a[t][r] * uu : 0.f;
-                    }
-                }
-            }
+        if (p.mask_bits && threadIdx.x < nt) {
+            const int t = threadIdx.x;
+            const int pr = off + t0 + t;
+            const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
+            p.mask_bits[row * p.W + (r0 >> 5)] = s_mask[t];
+            if (c == 0)
+                for (int wd = Ie / 32; wd < p.W; ++wd) p.mask_bits[row * p.W + wd] = 0u;
         }
-
-        // ---- masks of the tile's (token, slot) rows, and the union ---------
-        if (p.mask_bits) {
-            for (int i = threadIdx.x; i < nt * nwords; i += blockDim.x) {
-                const int t = i / nwords, wd = i - t * nwords;
-                const int pr = off + t0 + t;
-                const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
-                p.mask_bits[row * p.W + (r0 >> 5) + wd] = s_mask[t][wd];
-            }
-            // words past this expert's last row (experts narrower than Imax)
-            const int wtail = p.W - Ie / 32;
-            if (c == 0 && wtail > 0) {
-                for (int i = threadIdx.x; i < nt * wtail; i += blockDim.x) {
-                    const int t = i / wtail, wd = Ie / 32 + (i - t * wtail);
-                    const int pr = off + t0 + t;
-                    const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
-                    p.mask_bits[row * p.W + wd] = 0u;
-                }
-            }
-        }
-        if (threadIdx.x < nwords) s_union[threadIdx.x] |= s_act[threadIdx.x];
+        uni |= act;
+        __syncthreads();  // LDS is rewritten by the next tile
     }
-    if (MODE == kModeScore) return;
-    __syncthreads();
-    if (threadIdx.x < nwords) p.union_words[(size_t)xe * p.W + (r0 >> 5) + threadIdx.x] = s_union[threadIdx.x];
+    if (MODE != kModeScore && threadIdx.x == 0) p.union_words[(size_t)xe * p.W + (r0 >> 5)] = uni;
 }
 
 // ---------------------------------------------------------------------------
-template <class Tr, int NS, int TT>
+template <class Tr, int NW, int NSW, int TT>
 static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
 {
-    const dim3 grid(pl.max_touched * pl.C), block(256);
-    if (mode == MOE_SPARSE) hipLaunchKernelGGL((k_proj<Tr, NS, TT, MOE_SPARSE>), grid, block, 0, st, pp);
-    else if (mode == MOE_DENSE) hipLaunchKernelGGL((k_proj<Tr, NS, TT, MOE_DENSE>), grid, block, 0, st, pp);
-    else hipLaunchKernelGGL((k_proj<Tr, NS, TT, kModeScore>), grid, block, 0, st, pp);
+    const dim3 grid(pl.max_touched * pl.C), block(NW * kWave);
+    if (mode == MOE_SPARSE) hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MOE_SPARSE>), grid, block, 0, st, pp);
+    else if (mode == MOE_DENSE) hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MOE_DENSE>), grid, block, 0, st, pp);
+    else hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, kModeScore>), grid, block, 0, st, pp);
     return hipGetLastError();
 }
 
-template <class Tr, int NS>
+template <class Tr, int NW, int NSW>
 static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
 {
-    // the register tile holds TT * NS vectors of x; keep it at <= 32
     switch (pl.TT) {
-    case 1: return launch_proj_t<Tr, NS, 1>(pl, pp, mode, st);
-    case 2: if constexpr (NS <= 16) return launch_proj_t<Tr, NS, 2>(pl, pp, mode, st); break;
-    case 4: if constexpr (NS <= 8) return launch_proj_t<Tr, NS, 4>(pl, pp, mode, st); break;
-    case 8: if constexpr (NS <= 4) return launch_proj_t<Tr, NS, 8>(pl, pp, mode, st); break;
+    case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mode, st);
+    case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mode, st);
+    case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mode, st);
+    case 8: if constexpr (NSW <= 2) return launch_proj_t<Tr, NW, NSW, 8>(pl, pp, mode, st); break;
     }
     return hipErrorInvalidValue;
 }
@@ -226,12 +251,13 @@ static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, int mode,
 template <class Tr>
 static hipError_t launch_proj_tr(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
 {
+    // NS 16-byte vectors per lane per row, split over up to 4 wavefronts
     switch (pl.NS) {
-    case 1: return launch_proj_ns<Tr, 1>(pl, pp, mode, st);
-    case 2: return launch_proj_ns<Tr, 2>(pl, pp, mode, st);
-    case 4: return launch_proj_ns<Tr, 4>(pl, pp, mode, st);
-    case 8: return launch_proj_ns<Tr, 8>(pl, pp, mode, st);
-    case 16: return launch_proj_ns<Tr, 16>(pl, pp, mode, st);
+    case 1: return launch_proj_ns<Tr, 1, 1>(pl, pp, mode, st);
+    case 2: return launch_proj_ns<Tr, 2, 1>(pl, pp, mode, st);
+    case 4: return launch_proj_ns<Tr, 4, 1>(pl, pp, mode, st);
+    case 8: return launch_proj_ns<Tr, 4, 2>(pl, pp, mode, st);
+    case 16: return launch_proj_ns<Tr, 4, 4>(pl, pp, mode, st);
     }
     return hipErrorInvalidValue;
 }

@@ -49,28 +49,32 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
     float sel_sum = 0.f;
     for (int k = 0; k < K; ++k) {
         // lane-local best available expert
-        float bv = -INFINITY;
+        float bv = -INFINITY, braw = 0.f;
         int bid = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = lane + kWave * i;
             if (((avail >> i) & 1u) && (bid == 0x7fffffff || v[i] > bv)) {
                 bv = v[i];
+                braw = raw[i];
                 bid = e;
             }
         }
-        // wavefront arg-max: larger value, then lower id
+        // wavefront arg-max: larger value, then lower id (the raw logit rides
+        // along, so no dependent memory load is needed per round)
 #pragma unroll
         for (int s = 32; s >= 1; s >>= 1) {
             const float ov = __shfl_xor(bv, s, kWave);
+            const float oraw = __shfl_xor(braw, s, kWave);
             const int oid = __shfl_xor(bid, s, kWave);
             if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > bv || (ov == bv && oid < bid))) {
                 bv = ov;
+                braw = oraw;
                 bid = oid;
             }
         }
         if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
-        const float ev = expf(l[bid] - m);  // the chosen logit, as given
+        const float ev = expf(braw - m);
         if (lane == k) chosen_e = ev;
         sel_sum += ev;
         if (lane == 0) ids[(size_t)t * K + k] = bid;

@@ -160,11 +160,12 @@ def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, re
     if "y" not in o:
         o["y"] = torch.empty((T, H), dtype=torch.float32, device=dev)
     if want_masks:
-        o.setdefault("mask_bits", torch.empty((T, K + S, W), dtype=torch.int32, device=dev))
-        o.setdefault("union_idx", torch.empty((E + S, Imax), dtype=torch.int32, device=dev))
-        o.setdefault("union_cnt", torch.empty((E + S,), dtype=torch.int32, device=dev))
-        o.setdefault("topk_ids", torch.empty((T, K), dtype=torch.int32, device=dev))
-        o.setdefault("topk_w", torch.empty((T, K), dtype=torch.float32, device=dev))
+        shapes = dict(mask_bits=((T, K + S, W), torch.int32), union_idx=((E + S, Imax), torch.int32),
+                      union_cnt=((E + S,), torch.int32), topk_ids=((T, K), torch.int32),
+                      topk_w=((T, K), torch.float32))
+        for k, (shp, dt) in shapes.items():
+            if k not in o:
+                o[k] = torch.empty(shp, dtype=dt, device=dev)
     need = workspace_size(shape, mode)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)

@@ -156,7 +156,7 @@ def test_qwen_prefill_sampled(q):
 @pytest.mark.parametrize("over,T", [
     ((("E", 4), ("K", 4)), 5),                                      # K = E
     ((("E", 300), ("K", 3), ("I", 64)), 50),                        # many experts
-    ((("H", 512), ("E", 6), ("I", 96)), 7),                         # H = 512 (one vector per lane)
+    ((("H", 512), ("E", 6), ("I", 96), ("K", 2)), 7),               # H = 512 (one vector per lane)
     ((("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 3),              # H = 8192 (16 vectors per lane)
 ])
 def test_edge_shapes_bf16(over, T):
