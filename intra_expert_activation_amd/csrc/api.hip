@@ -78,7 +78,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->NCT = p->NS;
     const long long base = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT;
     long long split = (1024 + base - 1) / base;
-    if (split > 32) split = 32;
+    if (split > 8) split = 8;  // the combine adds NSPLIT partials per (token, slot)
     if (split < 1) split = 1;
     p->NSPLIT = (int)split;
 

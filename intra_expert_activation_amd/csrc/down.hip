@@ -226,37 +226,51 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream
 
 // ---------------------------------------------------------------------------
 // k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)],
-// each o being the fixed-order sum of the NSPLIT partials.  One thread per 4
-// columns of one token.
+// with o the sum of the NSPLIT partials.  A workgroup covers one token and 256
+// columns: 64 column quads x 4 thread groups; group g adds the terms
+// (slot, split) with (slot * NSPLIT + split) % 4 == g, and the 4 group sums
+// meet in LDS in a fixed order (so the result is deterministic).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(CombineParams p)
 {
+    __shared__ float4 s_acc[3][64];
     const int t = blockIdx.x;
-    const int c4 = blockIdx.y * blockDim.x + threadIdx.x;
+    const int q = threadIdx.x & 63;  // column quad within the block
+    const int g = threadIdx.x >> 6;  // term group
+    const int c4 = blockIdx.y * 64 + q;
     const int H4 = p.H / 4;
-    if (c4 >= H4) return;
+    const bool live = c4 < H4;
+    const int nterms = p.slots * p.NSPLIT;
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < p.slots; ++k) {
-        const int pr = p.pos[(size_t)t * p.slots + k];
-        const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < p.NSPLIT; ++sp) {
+    if (live) {
+        for (int i = g; i < nterms; i += 4) {
+            const int k = i / p.NSPLIT, sp = i - k * p.NSPLIT;
+            const int pr = p.pos[(size_t)t * p.slots + k];
+            const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
             const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)sp * p.P + pr) * p.H)[c4];
-            o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+            y.x = fmaf(wk, v.x, y.x);
+            y.y = fmaf(wk, v.y, y.y);
+            y.z = fmaf(wk, v.z, y.z);
+            y.w = fmaf(wk, v.w, y.w);
         }
-        y.x = fmaf(wk, o.x, y.x);
-        y.y = fmaf(wk, o.y, y.y);
-        y.z = fmaf(wk, o.z, y.z);
-        y.w = fmaf(wk, o.w, y.w);
     }
-    reinterpret_cast<float4 *>(p.y + (size_t)t * p.H)[c4] = y;
+    if (g > 0) s_acc[g - 1][q] = y;
+    __syncthreads();
+    if (g == 0 && live) {
+        const float4 a = s_acc[0][q], b = s_acc[1][q], c = s_acc[2][q];
+        y.x = (y.x + a.x) + (b.x + c.x);
+        y.y = (y.y + a.y) + (b.y + c.y);
+        y.z = (y.z + a.z) + (b.z + c.z);
+        y.w = (y.w + a.w) + (b.w + c.w);
+        reinterpret_cast<float4 *>(p.y + (size_t)t * p.H)[c4] = y;
+    }
 }
 
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
     const int H4 = pl.H / 4;
-    hipLaunchKernelGGL(k_combine, dim3(pl.T, (H4 + 255) / 256), dim3(256), 0, st, cp);
+    hipLaunchKernelGGL(k_combine, dim3(pl.T, (H4 + 63) / 64), dim3(256), 0, st, cp);
     return hipGetLastError();
 }
 

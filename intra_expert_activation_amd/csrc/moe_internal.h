@@ -167,13 +167,6 @@ struct F32 {
     static __device__ __forceinline__ V zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 };
 
-// Sum over the 64 lanes of a wavefront; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
 // SiLU(g) = g * sigmoid(g).  exp(-g) overflows to +inf for g < -88, giving
 // g / inf = -0, the correct limit.
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }

@@ -5,6 +5,7 @@
 // 2605.08575, Technical Summary, Methodology: router logic preserved); the
 // grouping is what lets every expert process its tokens as one batch.
 #include "moe_internal.h"
+#include "wave_reduce.h"
 
 namespace moe {
 
@@ -37,47 +38,36 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
         if ((avail >> i) & 1u) m = fmaxf(m, v[i]);
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, kWave));
+    m = wave_max(m);
     float denom = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
         if ((avail >> i) & 1u) denom += expf(raw[i] - m);
-    denom = wave_sum(denom);
+    denom = wave_sum_all(denom);
 
     float chosen_e = 0.f;  // lane k keeps exp(l - m) of slot k
     float sel_sum = 0.f;
     for (int k = 0; k < K; ++k) {
-        // lane-local best available expert
+        // lane-local best available expert (ascending ids: ties keep the lower)
         float bv = -INFINITY, braw = 0.f;
         int bid = 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-            const int e = lane + kWave * i;
             if (((avail >> i) & 1u) && (bid == 0x7fffffff || v[i] > bv)) {
                 bv = v[i];
                 braw = raw[i];
-                bid = e;
+                bid = lane + kWave * i;
             }
         }
-        // wavefront arg-max: larger value, then lower id (the raw logit rides
-        // along, so no dependent memory load is needed per round)
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) {
-            const float ov = __shfl_xor(bv, s, kWave);
-            const float oraw = __shfl_xor(braw, s, kWave);
-            const int oid = __shfl_xor(bid, s, kWave);
-            if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > bv || (ov == bv && oid < bid))) {
-                bv = ov;
-                braw = oraw;
-                bid = oid;
-            }
-        }
-        if ((bid & (kWave - 1)) == lane) avail &= ~(1u << (bid / kWave));
-        const float ev = expf(braw - m);
+        // wavefront arg-max: the largest value, then the lowest id holding it
+        const float top = wave_max(bid == 0x7fffffff ? -INFINITY : bv);
+        const int win = wave_min((bid != 0x7fffffff && bv == top) ? bid : 0x7fffffff);
+        const float wraw = __shfl(braw, win & (kWave - 1), kWave);  // the chosen logit, as given
+        if ((win & (kWave - 1)) == lane) avail &= ~(1u << (win / kWave));
+        const float ev = expf(wraw - m);
         if (lane == k) chosen_e = ev;
         sel_sum += ev;
-        if (lane == 0) ids[(size_t)t * K + k] = bid;
+        if (lane == 0) ids[(size_t)t * K + k] = win;
     }
     if (lane < K) {
         const float p = chosen_e / denom;

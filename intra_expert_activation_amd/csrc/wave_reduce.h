@@ -123,4 +123,53 @@ __device__ __forceinline__ bool xreduce_owner(int lane)
     return (lane & ((1 << low_bits) - 1)) == 0;
 }
 
+
+// Wavefront-wide max / min of one value, result in every lane (same stages as
+// fold: permlane swaps for lane bits 5 and 4, DPP for bits 3..0).
+template <int B, class Op>
+__device__ __forceinline__ uint32_t fold_bits(uint32_t x, Op op)
+{
+    if constexpr (B == 5) {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return op(r[0], r[1]);
+    } else if constexpr (B == 4) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return op(r[0], r[1]);
+    } else {
+        constexpr int C = B == 3 ? kDppRowMirror : B == 2 ? kDppRowHalfMirror : B == 1 ? kDppXor2 : kDppXor1;
+        return op(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, C, 0xf, 0xf, false));
+    }
+}
+
+template <class Op>
+__device__ __forceinline__ uint32_t wave_fold(uint32_t x, Op op)
+{
+    x = fold_bits<0>(x, op);
+    x = fold_bits<1>(x, op);
+    x = fold_bits<2>(x, op);
+    x = fold_bits<3>(x, op);
+    x = fold_bits<4>(x, op);
+    x = fold_bits<5>(x, op);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    return __uint_as_float(wave_fold(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+
+__device__ __forceinline__ int wave_min(int v)
+{
+    return (int)wave_fold((uint32_t)v, [](uint32_t a, uint32_t b) { return (int)a < (int)b ? a : b; });
+}
+
+__device__ __forceinline__ float wave_sum_all(float v)
+{
+    return __uint_as_float(wave_fold(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+
 }  // namespace moe
