@@ -82,6 +82,20 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     if (split < 1) split = 1;
     p->NSPLIT = (int)split;
 
+    // MFMA path: bf16 experts with at least kMfmaMinPairs pairs.  A routed
+    // expert has at most T pairs, so with T below the threshold it is off.
+    p->nm = INT_MAX;
+    p->use_mfma = 0;
+    p->NT = (p->Imax + 63) / 64;
+    p->max_items = 0;
+    if (!calib && p->dtype == MOE_BF16 && T >= kMfmaMinPairs) {
+        p->nm = kMfmaMinPairs;
+        p->use_mfma = 1;
+        // sum over experts of ceil(n_e / 64) <= A/64 + (number of such experts)
+        const int big = (p->A / p->nm < p->E ? p->A / p->nm : p->E);
+        p->max_items = p->A / kMfmaTokens + big + p->S * ((T + kMfmaTokens - 1) / kMfmaTokens);
+    }
+
     // workspace layout
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -102,6 +116,12 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
     p->off_partial = take(calib ? 0 : (size_t)p->NSPLIT * p->P * p->H * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
+    const size_t blocks = (size_t)p->max_items * p->NT;
+    p->off_items = take((size_t)p->max_items * 4);
+    p->off_nact = take(blocks * 4);
+    p->off_list = take(blocks * 64);
+    p->off_hhi = take(blocks * 64 * 64 * 2);
+    p->off_hlo = take(blocks * 64 * 64 * 2);
     p->total = o;
     return MOE_OK;
 }
@@ -210,6 +230,10 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos;
     gp.union_cnt = a->union_cnt;
+    gp.union_words = union_words;
+    gp.W = pl.W;
+    gp.nm = pl.nm;
+    gp.items = ws_at<int32_t>(ws, pl.off_items);
     if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
@@ -220,9 +244,27 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     pp.h = h; pp.mask_bits = a->mask_bits; pp.union_words = union_words;
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
     pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
+    pp.nm = pl.nm;
+
+    MfmaParams mp{};
+    mp.x = (const uint16_t *)a->x;
+    mp.wg = (const uint16_t *)a->w_gate; mp.wu = (const uint16_t *)a->w_up; mp.wd = (const uint16_t *)a->w_down;
+    mp.swg = (const uint16_t *)a->ws_gate; mp.swu = (const uint16_t *)a->ws_up; mp.swd = (const uint16_t *)a->ws_down;
+    mp.tau = a->tau;
+    mp.hdr = hdr; mp.counts = counts; mp.offsets = offsets; mp.items = ws_at<int32_t>(ws, pl.off_items);
+    mp.pair_tok = pair_tok; mp.pair_slot = pair_slot;
+    mp.hhi = ws_at<uint16_t>(ws, pl.off_hhi); mp.hlo = ws_at<uint16_t>(ws, pl.off_hlo);
+    mp.nact = ws_at<int32_t>(ws, pl.off_nact); mp.list = ws_at<uint8_t>(ws, pl.off_list);
+    mp.mask_bits = a->mask_bits; mp.union_words = union_words; mp.partial = partial;
+    mp.union_idx = a->union_idx; mp.union_cnt = a->union_cnt;
+    mp.H = pl.H; mp.E = pl.E; mp.I = pl.I; mp.Is = pl.Is; mp.S = pl.S; mp.W = pl.W; mp.Imax = pl.Imax;
+    mp.slots = pl.slots; mp.NT = pl.NT; mp.max_items = pl.max_items;
+
+    // the events bracket the expert projection (gate, score, mask, up) of both paths
     if (a->prof_event_begin && hipEventRecord((hipEvent_t)a->prof_event_begin, stream) != hipSuccess)
         return MOE_ERR_HIP;
     if (launch_proj(pl, pp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_proj_mfma(pl, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
     if (a->prof_event_end && hipEventRecord((hipEvent_t)a->prof_event_end, stream) != hipSuccess)
         return MOE_ERR_HIP;
 
@@ -233,11 +275,14 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     dp.union_idx = a->union_idx; dp.union_cnt = a->union_cnt;
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
     dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.NSPLIT = pl.NSPLIT;
+    dp.nm = pl.nm;
     if (launch_down(pl, dp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_down_mfma(pl, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
-    cp.partial = partial; cp.topk_w = w; cp.pos = pos; cp.y = a->y;
-    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NSPLIT = pl.NSPLIT;
+    cp.partial = partial; cp.topk_w = w; cp.topk_ids = ids; cp.counts = counts; cp.pos = pos; cp.y = a->y;
+    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.E = pl.E; cp.slots = pl.slots; cp.P = pl.P;
+    cp.NSPLIT = pl.NSPLIT; cp.nm = pl.nm;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -280,6 +325,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos; gp.union_cnt = nullptr;
+    gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr;
     if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
@@ -290,6 +336,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     pp.h = scores; pp.mask_bits = nullptr; pp.union_words = nullptr;
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
     pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
+    pp.nm = pl.nm;  // INT_MAX: every expert is scored by the GEMV kernel
     if (launch_proj(pl, pp, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
 
     SelectParams sp{};

@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
     const int n = p.counts[xe];
+    if (n >= p.nm) return;  // this expert takes the MFMA path
     const int off = p.offsets[xe];
     const int rowV = p.NCT * kWave;
     const int lane = threadIdx.x & (kWave - 1);
@@ -226,7 +227,8 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream
 
 // ---------------------------------------------------------------------------
 // k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)],
-// with o the sum of the NSPLIT partials.  A workgroup covers one token and 256
+// with o the sum of the NSPLIT partials (one partial for an expert on the MFMA
+// path).  A workgroup covers one token and 256
 // columns: 64 column quads x 4 thread groups; group g adds the terms
 // (slot, split) with (slot * NSPLIT + split) % 4 == g, and the 4 group sums
 // meet in LDS in a fixed order (so the result is deterministic).
@@ -245,6 +247,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p)
     if (live) {
         for (int i = g; i < nterms; i += 4) {
             const int k = i / p.NSPLIT, sp = i - k * p.NSPLIT;
+            const int e = (k < p.K) ? p.topk_ids[(size_t)t * p.K + k] : p.E + (k - p.K);
+            if (sp > 0 && p.counts[e] >= p.nm) continue;  // MFMA experts write split 0 only
             const int pr = p.pos[(size_t)t * p.slots + k];
             const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
             const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)sp * p.P + pr) * p.H)[c4];

@@ -15,6 +15,8 @@ constexpr int kMaxExperts = 512;   // E + S
 constexpr int kMaxK = 32;
 constexpr int kMaxRows = 16384;    // I, I_shared
 constexpr int kMaxRowsPerChunk = 256;
+constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
+constexpr int kMfmaMinPairs = 32;  // default pair-count threshold of the MFMA path
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a
@@ -39,10 +41,16 @@ struct Plan {
     // down projection kernel
     int NCT;         // column tiles: H / (64 * epl)
     int NSPLIT;      // splits of an expert's union rows (deterministic split-K)
+    // MFMA path for experts with at least `nm` pairs (bf16 only)
+    int use_mfma;    // 0 when no expert can reach nm (T < nm) or for fp32 / scores
+    int nm;          // pair-count threshold (INT_MAX when the path is off)
+    int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
+    int max_items;   // upper bound on (expert, 64-token tile) work items
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched;
     size_t off_pair_tok, off_pair_slot, off_pos, off_union, off_h, off_partial;
     size_t off_taus;
+    size_t off_items, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
 };
 
@@ -64,6 +72,10 @@ struct GroupParams {
     int32_t *pair_slot;   // [P] slot of the pair
     int32_t *pos;         // [T*slots] grouped position of (t, slot)
     int32_t *union_cnt;   // optional output, zeroed for untouched experts
+    uint32_t *union_words;// [EX,W], zeroed for the experts on the MFMA path
+    int W;
+    int nm;               // MFMA pair-count threshold
+    int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
 };
 
 struct ProjParams {
@@ -75,6 +87,7 @@ struct ProjParams {
     uint32_t *mask_bits;  // optional output [T,slots,W]
     uint32_t *union_words;// [EX,W]
     int H, E, I, Is, S, K, A, W, slots, C, R;
+    int nm;               // experts with nm or more pairs take the MFMA path
 };
 
 struct DownParams {
@@ -86,14 +99,30 @@ struct DownParams {
     int32_t *union_idx;   // optional output [EX, Imax]
     int32_t *union_cnt;   // optional output [EX]
     int H, E, I, Is, S, A, P, W, Imax, NCT, NSPLIT;
+    int nm;
 };
 
 struct CombineParams {
     const float *partial;
     const float *topk_w;
+    const int32_t *topk_ids, *counts;
     const int32_t *pos;
     float *y;
-    int T, H, K, slots, P, NSPLIT;
+    int T, H, K, E, slots, P, NSPLIT;
+    int nm;               // MFMA experts write one partial instead of NSPLIT
+};
+
+struct MfmaParams {
+    const uint16_t *x, *wg, *wu, *wd, *swg, *swu, *swd;
+    const float *tau;
+    const int32_t *hdr, *counts, *offsets, *items, *pair_tok, *pair_slot;
+    uint16_t *hhi, *hlo;  // compacted h per (item, neuron tile): [64 tokens][64] bf16 hi / lo
+    int32_t *nact;        // active rows per (item, neuron tile)
+    uint8_t *list;        // their offsets within the tile, ascending
+    uint32_t *mask_bits, *union_words;
+    float *partial;
+    int32_t *union_idx, *union_cnt;
+    int H, E, I, Is, S, W, Imax, slots, NT, max_items;
 };
 
 struct SelectParams {
@@ -116,6 +145,8 @@ hipError_t launch_proj(const Plan &pl, const ProjParams &pp, int mode, hipStream
 hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream_t stream);
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t stream);
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
+hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
+hipError_t launch_down_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -110,6 +110,7 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
     const int r0 = c * kChunk;
     if (r0 >= Ie) return;
     const int n = p.counts[xe];
+    if (n >= p.nm) return;  // this expert takes the MFMA path
     const int off = p.offsets[xe];
     constexpr int rowV = NW * NSW * kWave;  // 16-byte vectors per row (H / epl)
     const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;

@@ -207,8 +207,36 @@ __global__ __launch_bounds__(1024) void k_group(GroupParams p)
         if (lane == kWave - 1) {
             p.hdr[0] = tincl;
         }
+        // MFMA work items: (expert, 64-token tile) of every expert with at
+        // least nm pairs, ascending expert then tile
+        int tiles = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX && loc[i] >= p.nm) tiles += (loc[i] + kMfmaTokens - 1) / kMfmaTokens;
+        }
+        int iincl = tiles;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(iincl, s, kWave);
+            if (lane >= s) iincl += o;
+        }
+        int ipos = iincl - tiles;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX && loc[i] >= p.nm)
+                for (int tl = 0; tl < (loc[i] + kMfmaTokens - 1) / kMfmaTokens; ++tl) p.items[ipos++] = (e << 16) | tl;
+        }
+        if (lane == kWave - 1) p.hdr[1] = iincl;
     }
     __syncthreads();
+    // union words of the MFMA experts are built with atomic ORs: clear them
+    if (p.union_words)
+        for (int i = tid; i < EX * p.W; i += blockDim.x) {
+            const int e = i / p.W;
+            if (s_off[e + 1] - s_off[e] >= p.nm) p.union_words[i] = 0u;
+        }
 
     // pass 2: stable scatter of the routed pairs
     for (int base = a_begin; base < a_end; base += kWave) {
