@@ -31,9 +31,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec at 1 MI355X + HBM GB/s fraction; speedup vs dense"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 ROTATE = 16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_projection_qwen_decode_T64.json")
 KERNEL_SRC = os.path.join(ROOT, "intra_expert_activation_amd", "csrc", "proj.hip")
+
+
+# name: (config id, default batch, default q, default sweep, description)
+WORKLOADS = {
+    "decode": (2, 64, 0.85, "1,8,32", "qwen-moe-style decode layer: H 2048, 128 experts x I 768, top-8"),
+    "prefill": (5, 4096, 0.70, "", "qwen-moe-style prefill layer: H 2048, 128 experts x I 768, top-8"),
+    "mixtral": (3, 16, 0.90, "1,128", "mixtral-style layer: H 4096, 8 experts x I 14336, top-2"),
+    "deepseek": (4, 64, 0.85, "1,8,32", "deepseek-v2-lite-style layer: H 2048, 64 experts x I 1408 top-6 "
+                                          "+ 2 shared experts, zipf routing"),
+}
 
 
 def parse():
@@ -41,13 +52,28 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--tokens", type=int, default=64)
-    ap.add_argument("--q", type=float, default=0.85)
-    ap.add_argument("--sweep", default="1,8,32", help="extra batch sizes reported beside the headline")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="decode")
+    ap.add_argument("--tokens", type=int, default=None, help="batch size (default: the workload's)")
+    ap.add_argument("--q", type=float, default=None, help="target sparsity of the calibration")
+    ap.add_argument("--sweep", default=None, help="extra batch sizes reported beside the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 5 plain device copies of this many bytes (HBM counter scale)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """A plain device-to-device copy of known size, used to scale HBM counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 5}))
 
 
 def main():
@@ -57,6 +83,9 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only: run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_bytes:
+        copy_probe(args.copy_bytes)
+        return
 
     import torch
 
@@ -68,11 +97,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    c = synth.config(2)
+    cfg_id, T_def, q_def, sweep_def, desc = WORKLOADS[args.workload]
+    T = args.tokens or T_def
+    args.q = q_def if args.q is None else args.q
+    args.sweep = sweep_def if args.sweep is None else args.sweep
+    c = synth.config(cfg_id)
+    rotate = ROTATE if T <= 256 else 2
     t_gen = time.time()
     L = synth.make_layer(c)
-    T = args.tokens
-    x_all, l_all = synth.make_tokens(c, 2, ROTATE * max(T, 64))
+    x_all, l_all = synth.make_tokens(c, 2, rotate * max(T, max(c["T"])))
     xc, lc = synth.make_tokens(c, 1)
     gen_s = time.time() - t_gen
 
@@ -80,53 +113,62 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     Wg, Wu, Wd = bf16(L["w_gate"]), bf16(L["w_up"]), bf16(L["w_down"])
-    H, E, I, K = L["H"], L["E"], L["I"], L["K"]
-    tau = moe.calibrate_threshold(bf16(xc), torch.from_numpy(lc).to(dev), Wg, args.q, K=K)
+    H, E, I, K, S, Is = L["H"], L["E"], L["I"], L["K"], L["S"], L["I_shared"]
+    renorm = bool(L["renormalize"])
+    shared = (bf16(L["ws_gate"]), bf16(L["ws_up"]), bf16(L["ws_down"])) if S else None
+    Imax = max(I, Is) if S else I
+    rows = np.array([I] * E + [Is] * S)
+    tau = moe.calibrate_threshold(bf16(xc), torch.from_numpy(lc).to(dev), Wg, args.q, K=K,
+                                  shared_gate=shared[0] if S else None)
     torch.cuda.synchronize()
 
     def batches(Tb):
         out = []
-        for r in range(ROTATE):
+        for r in range(rotate):
             sl = slice(r * Tb, (r + 1) * Tb)
             out.append((bf16(x_all[sl]), torch.from_numpy(np.ascontiguousarray(l_all[sl])).to(dev)))
         return out
 
     def make_outputs(Tb):
-        S = 0
         return dict(y=torch.empty((Tb, H), dtype=torch.float32, device=dev),
-                    mask_bits=torch.empty((Tb, K + S, I // 32), dtype=torch.int32, device=dev),
-                    union_idx=torch.empty((E, I), dtype=torch.int32, device=dev),
-                    union_cnt=torch.empty((E,), dtype=torch.int32, device=dev),
+                    mask_bits=torch.empty((Tb, K + S, Imax // 32), dtype=torch.int32, device=dev),
+                    union_idx=torch.empty((E + S, Imax), dtype=torch.int32, device=dev),
+                    union_cnt=torch.empty((E + S,), dtype=torch.int32, device=dev),
                     topk_ids=torch.empty((Tb, K), dtype=torch.int32, device=dev),
                     topk_w=torch.empty((Tb, K), dtype=torch.float32, device=dev))
 
     def run(Tb, mode, steps, warmup, kernel_timing, graph):
         bs = batches(Tb)
-        outs = [make_outputs(Tb) for _ in range(ROTATE)]
-        shape = moe.layer_shape(bs[0][0], Wg, K, True)
+        outs = [make_outputs(Tb) for _ in range(rotate)]
+        shape = moe.layer_shape(bs[0][0], Wg, K, renorm, shared[0] if S else None)
         ws = moe.alloc_workspace(moe.workspace_size(shape, mode), dev)
 
         def call(r, ev=None):
             x, lg = bs[r]
-            moe.sparse_expert_ffn(x, lg, Wg, Wu, Wd, tau, K=K, mode=mode, out=outs[r], workspace=ws,
-                                  prof_events=ev)
+            moe.sparse_expert_ffn(x, lg, Wg, Wu, Wd, tau, K=K, renormalize=renorm, shared=shared, mode=mode,
+                                  out=outs[r], workspace=ws, prof_events=ev)
 
-        # per-batch algorithmic bytes from the returned unions
-        for r in range(ROTATE):
+        # per-batch algorithmic bytes and flops from the returned unions
+        for r in range(rotate):
             call(r)
         torch.cuda.synchronize()
-        ucnt = [outs[r]["union_cnt"].cpu().numpy() for r in range(ROTATE)]
-        ids = [outs[r]["topk_ids"].cpu().numpy() for r in range(ROTATE)]
-        touched = [np.unique(i) for i in ids]
-        ub = [int(ucnt[r][touched[r]].sum()) if mode == moe.MOE_SPARSE else int(len(touched[r]) * I)
-              for r in range(ROTATE)]
-        proj_bytes = [(len(touched[r]) * I + ub[r]) * H * 2 + Tb * H * 2 for r in range(ROTATE)]
-        call_bytes = [(len(touched[r]) * I + 2 * ub[r]) * H * 2 + Tb * H * 2 + Tb * E * 4 + Tb * H * 4
-                      for r in range(ROTATE)]
-        active = float(np.mean([ub[r] / (len(touched[r]) * I) for r in range(ROTATE)]))
+        proj_bytes, call_bytes, proj_flops, call_flops, active = [], [], [], [], []
+        for r in range(rotate):
+            ucnt = outs[r]["union_cnt"].cpu().numpy().astype(np.int64)
+            ne = np.bincount(outs[r]["topk_ids"].cpu().numpy().ravel(), minlength=E + S).astype(np.int64)
+            ne[E:] = Tb
+            t = ne > 0
+            u = ucnt if mode == moe.MOE_SPARSE else rows
+            gate_rows, union_rows = int(rows[t].sum()), int(u[t].sum())
+            proj_bytes.append((gate_rows + union_rows) * H * 2 + Tb * H * 2)
+            call_bytes.append((gate_rows + 2 * union_rows) * H * 2 + Tb * H * 2 + Tb * E * 4 + Tb * H * 4)
+            proj_flops.append(float((2 * H * ne * (rows + u))[t].sum()))
+            call_flops.append(float((2 * H * ne * (rows + 2 * u))[t].sum()))
+            active.append(union_rows / gate_rows)
+        active = float(np.mean(active))
 
         for s in range(warmup):
-            call(s % ROTATE)
+            call(s % rotate)
         torch.cuda.synchronize()
 
         graphs = None
@@ -136,13 +178,13 @@ def main():
                 st = torch.cuda.Stream()
                 st.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(st):
-                    for r in range(ROTATE):
+                    for r in range(rotate):
                         g = torch.cuda.CUDAGraph()
                         with torch.cuda.graph(g, stream=st):
                             call(r)
                         graphs.append(g)
                 torch.cuda.current_stream().wait_stream(st)
-                for r in range(ROTATE):
+                for r in range(rotate):
                     graphs[r].replay()
                 torch.cuda.synchronize()
             except Exception as exc:  # capture unsupported: time eager calls
@@ -153,7 +195,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(steps):
-            r = s % ROTATE
+            r = s % rotate
             if timers is not None:
                 call(r, timers[s].events)
             elif graphs is not None:
@@ -164,15 +206,19 @@ def main():
         elapsed = time.perf_counter() - t0
         res = dict(ms_per_step=elapsed * 1e3 / steps, tokens_per_s=Tb * steps / elapsed,
                    call_bytes=float(np.mean(call_bytes)), proj_bytes=float(np.mean(proj_bytes)),
+                   proj_flops=float(np.mean(proj_flops)), call_flops=float(np.mean(call_flops)),
                    union_fraction=active, graph=graphs is not None and timers is None)
         if timers is not None:
             kms = np.array([t.elapsed_ms() for t in timers])
             for t in timers:
                 t.close()
-            kb = np.array([proj_bytes[s % ROTATE] for s in range(steps)])
+            kb = np.array([proj_bytes[s % rotate] for s in range(steps)])
+            kf = np.array([proj_flops[s % rotate] for s in range(steps)])
             res["proj_ms"] = float(kms.mean())
-            res["proj_gbs"] = float((kb / (kms * 1e-3)).mean() / 1e9)
+            res["proj_gbs"] = float(kb.sum() / (kms.sum() * 1e-3) / 1e9)
+            res["proj_tflops"] = float(kf.sum() / (kms.sum() * 1e-3) / 1e12)
         res["call_gbs"] = res["call_bytes"] / (res["ms_per_step"] * 1e-3) / 1e9
+        res["call_tflops"] = res["call_flops"] / (res["ms_per_step"] * 1e-3) / 1e12
         return res
 
     use_graph = not args.no_graph
@@ -196,12 +242,24 @@ def main():
 
     best = head_g if head_g["ms_per_step"] < head["ms_per_step"] else head
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if args.workload == "decode" and T == 64 and os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
         src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
         if tr.get("kernel_src_sha256") == src_sha:
             traffic = tr.get("hbm_bytes_per_launch")
 
+    if T >= 1024:  # prefill: the projection is a dense contraction on MFMA
+        roof = {"bound": "mfma", "achieved": round(head["proj_tflops"], 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(head["proj_tflops"] / MFMA_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": "k_proj_mfma (gate, SiLU, threshold, ballot, up; bf16 MFMA)",
+                "kernel_avg_us": round(head["proj_ms"] * 1e3, 2),
+                "algorithmic_flops_per_launch": round(head["proj_flops"])}
+    else:
+        roof = {"bound": "hbm", "achieved": round(head["proj_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["proj_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "k_proj (gate, SiLU, threshold, ballot, up)",
+                "kernel_avg_us": round(head["proj_ms"] * 1e3, 2),
+                "algorithmic_bytes_per_launch": round(head["proj_bytes"])}
     line = {
         "metric": METRIC,
         "value": round(best["tokens_per_s"], 1),
@@ -215,50 +273,49 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"qwen-moe-style decode layer: H 2048, 128 experts x I 768, top-8, "
-                               f"T {T}, bf16 weights, tau at q={args.q}",
+        "config": {"workload": f"{desc}, T {T}, bf16 weights, tau at q={args.q}",
                    "global_batch": T, "q": args.q, "timing": "graph replay" if best["graph"] else "eager"},
-        "roofline": {"bound": "hbm", "achieved": round(head["proj_gbs"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["proj_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "k_proj (gate, SiLU, threshold, ballot, up)",
-                     "kernel_avg_us": round(head["proj_ms"] * 1e3, 2),
-                     "algorithmic_bytes_per_launch": round(head["proj_bytes"])},
+        "roofline": roof,
         "speedup_vs_dense": round(dense_g["ms_per_step"] / head_g["ms_per_step"], 3),
         "dense_ms_per_step": round(dense_g["ms_per_step"], 5),
-        "dense_proj_frac": round(dense_k["proj_gbs"] / HBM_PEAK_GBS, 4),
+        "dense_proj_frac": round((dense_k["proj_tflops"] / MFMA_PEAK_TFLOPS) if T >= 1024
+                                 else (dense_k["proj_gbs"] / HBM_PEAK_GBS), 4),
         "call_hbm_frac": round(head_g["call_gbs"] / HBM_PEAK_GBS, 4),
+        "call_tflops": round(head_g["call_tflops"], 1),
         "union_fraction": round(head["union_fraction"], 4),
         "sweep": sweep,
         "setup_s": round(gen_s, 1),
     }
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(L, c, x_all, l_all, xc, lc, T, args)
+        line["cpu_baseline"] = cpu_baseline(L, x_all, l_all, xc, lc, T, args)
 
     print(json.dumps(line))
 
 
-def cpu_baseline(L, c, x_all, l_all, xc, lc, T, args):
+def cpu_baseline(L, x_all, l_all, xc, lc, T, args):
     """The CPU oracle as it stands (float64 loops, OpenMP over tokens) on a
-    bounded sample of the same workload: whole T-token batches, repeated over
-    the rotation until about --cpu-seconds of work."""
+    bounded sample of the same workload: batches of min(T, 64) tokens of the
+    same draw, repeated until about --cpu-seconds of work."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or oracle.default_threads()
     threads = max(1, min(threads, oracle.default_threads()))
     tau = oracle.calibrate(L, xc, lc, args.q, threads=threads)
+    Tb = min(T, 64)
+    nb = x_all.shape[0] // Tb
     done, t0 = 0, time.perf_counter()
     r = 0
     while True:
-        sl = slice(r * T, (r + 1) * T)
+        sl = slice(r * Tb, (r + 1) * Tb)
         oracle.moe(L, x_all[sl], l_all[sl], tau, threads=threads)
-        done += T
-        r = (r + 1) % ROTATE
+        done += Tb
+        r = (r + 1) % nb
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     el = time.perf_counter() - t0
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done // T} batches of {T} tokens of the same layer (float64 oracle, sparse mode)"}
+            "sample": f"{done // Tb} batches of {Tb} tokens of the same layer (float64 oracle, sparse mode)"}
 
 
 if __name__ == "__main__":

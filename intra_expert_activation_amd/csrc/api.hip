@@ -63,15 +63,15 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->R = 32;
     p->C = p->Imax / 32;
 
-    // token tile: covers the mean pairs per touched routed expert; at most 8
-    // (the dot products of larger tiles outrun the weight stream), and at most
-    // 16 vectors of hidden states per lane (a wavefront holds NS/4 of a row)
-    const int touched_routed = p->A < p->E ? p->A : p->E;
-    const int mean_ne = touched_routed > 0 ? (p->A + touched_routed - 1) / touched_routed : 1;
+    // largest token tile: the kernels pick 1, 2, 4 or 8 per tile to cover an
+    // expert's remaining pairs, so its rows stream once when n_e <= TT.  At
+    // most 8 (the dot products of larger tiles outrun the weight stream) and
+    // at most 16 vectors of hidden states per lane (a wavefront holds NS/4 of
+    // a row); no expert has more than T pairs.
     const int nsw = p->NS <= 4 ? 1 : p->NS / 4;
     const int tt_cap = 16 / nsw < 8 ? 16 / nsw : 8;
     p->TT = 1;
-    while (p->TT < mean_ne && p->TT < tt_cap) p->TT *= 2;
+    while (p->TT < T && p->TT < tt_cap) p->TT *= 2;
 
     // down projection: column tiles of 64 lanes x 16 bytes; split the union
     // rows so the grid has ~1024 workgroups when few experts are touched

@@ -19,51 +19,145 @@
 
 namespace moe {
 
-template <class Tr, int UR, int TB>
-struct DownBatch {
-    typename Tr::V w[UR];
-    float h[UR][TB];
-};
+constexpr int kDownRowChunk = 256;  // rows of h staged in LDS at a time
 
-// Loads of the wavefront's next UR rows of the split: this lane's 16-byte
-// vector of each down row and the tile's h values of each row.
-template <class Tr, int UR, int TB, int MODE>
-__device__ __forceinline__ void load_down_batch(DownBatch<Tr, UR, TB> &bt, const typename Tr::V *Wd,
-                                                const float *hb, const uint16_t *list, int i0, int hi,
-                                                int n, int t0, int nt, int rowV)
+// Loads of the wavefront's next UR rows: this lane's 16-byte vector of each
+// down row (rows past `hi` read as zero).
+template <class Tr, int UR, int MODE>
+__device__ __forceinline__ void load_down_rows(typename Tr::V (&w)[UR], const typename Tr::V *Wd,
+                                               const uint16_t *list, int i0, int hi, int rowV)
 {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
         const int i = i0 + 4 * u;
         const int j = (i < hi) ? ((MODE == MOE_DENSE) ? i : (int)list[i]) : -1;
-        bt.w[u] = (j >= 0) ? Wd[(size_t)j * rowV] : Tr::zero();
-#pragma unroll
-        for (int t = 0; t < TB; ++t) bt.h[u][t] = (j >= 0 && t < nt) ? hb[(size_t)j * n + t0 + t] : 0.f;
+        w[u] = (j >= 0) ? Wd[(size_t)j * rowV] : Tr::zero();
     }
 }
 
+// acc[t][:] += h[row][t] * w[row][:] for the batch; h comes from LDS (one
+// broadcast read per 4 tokens), rows past the chunk contribute zero weights.
 template <class Tr, int UR, int TB>
-__device__ __forceinline__ void fma_down_batch(const DownBatch<Tr, UR, TB> &bt, float (&acc)[TB][Tr::kEpl])
+__device__ __forceinline__ void fma_down_rows(const typename Tr::V (&w)[UR], const float *s_h, int r0,
+                                              float (&acc)[TB][Tr::kEpl])
 {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
         float wf[Tr::kEpl];
-        Tr::unpack(bt.w[u], wf);
+        Tr::unpack(w[u], wf);
+        const float *hr = s_h + (size_t)(r0 + 4 * u) * TB;
+        float hv[TB];
+#pragma unroll
+        for (int t = 0; t < TB; t += (TB >= 4 ? 4 : TB)) {
+            if constexpr (TB >= 4) {
+                const float4 q = *reinterpret_cast<const float4 *>(hr + t);
+                hv[t] = q.x; hv[t + 1] = q.y; hv[t + 2] = q.z; hv[t + 3] = q.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < TB; ++k) hv[k] = hr[k];
+            }
+        }
 #pragma unroll
         for (int t = 0; t < TB; ++t)
 #pragma unroll
-            for (int e = 0; e < Tr::kEpl; ++e) acc[t][e] = fmaf(bt.h[u][t], wf[e], acc[t][e]);
+            for (int e = 0; e < Tr::kEpl; ++e) acc[t][e] = fmaf(hv[t], wf[e], acc[t][e]);
     }
 }
 
-template <class Tr, int TB, int MODE>
+// One token tile of TB tokens (nt valid): the split's rows of this column tile.
+// The tile's h values of the split's rows are staged in LDS, kDownRowChunk
+// rows at a time ([row][TB], zero past nt and past the split).
+template <class Tr, int TB, int TBMAX, int MODE>
+__device__ __forceinline__ void down_tile(const DownParams &p, float (&s_red)[2][TBMAX][kWave * Tr::kEpl],
+                                          float *s_h, const uint16_t *s_list, const typename Tr::V *Wd,
+                                          const float *hb, int n, int off, int t0, int nt, int lo, int hi,
+                                          int sp, int cv, int rowV, int lane, int wave)
+{
+    constexpr int EPL = Tr::kEpl;
+    constexpr int UR = 4;  // rows per batch per wavefront; two batches in flight
+    float acc[TB][EPL];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+
+    for (int c0 = lo; c0 < hi; c0 += kDownRowChunk) {
+        const int c1 = min(hi, c0 + kDownRowChunk);
+        // stage h[row][t] for rows c0..c1 (padded to a multiple of 4 * UR rows)
+        const int rows = ((c1 - c0 + 4 * UR - 1) / (4 * UR)) * (4 * UR);
+        for (int q = threadIdx.x; q < rows * TB; q += blockDim.x) {
+            const int r = q / TB, t = q - r * TB;
+            const int i = c0 + r;
+            float v = 0.f;
+            if (i < c1 && t < nt) {
+                const int j = (MODE == MOE_DENSE) ? i : (int)s_list[i];
+                v = hb[(size_t)j * n + t0 + t];
+            }
+            s_h[q] = v;
+        }
+        __syncthreads();
+        // rows c0 + wave + 4 i of the chunk, batches of UR, two in flight
+        const int mine = c1 - c0 - wave > 0 ? (c1 - c0 - wave + 3) / 4 : 0;
+        const int nb = (mine + UR - 1) / UR;
+        typename Tr::V A[UR], B[UR];
+        if (nb > 0) load_down_rows<Tr, UR, MODE>(A, Wd, s_list, c0 + wave, c1, rowV);
+#pragma unroll 1
+        for (int b = 0; b < nb; b += 2) {
+            if (b + 1 < nb) load_down_rows<Tr, UR, MODE>(B, Wd, s_list, c0 + wave + 4 * UR * (b + 1), c1, rowV);
+            fma_down_rows<Tr, UR, TB>(A, s_h, wave + 4 * UR * b, acc);
+            if (b + 1 >= nb) break;
+            if (b + 2 < nb) load_down_rows<Tr, UR, MODE>(A, Wd, s_list, c0 + wave + 4 * UR * (b + 2), c1, rowV);
+            fma_down_rows<Tr, UR, TB>(B, s_h, wave + 4 * UR * (b + 1), acc);
+        }
+        __syncthreads();  // s_h is rewritten by the next chunk
+    }
+
+    // wavefront sums in a fixed order: (w0 + w2) + (w1 + w3)
+    if (wave >= 2) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s_red[wave - 2][t][lane * EPL + e] = acc[t][e];
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[t][e] += s_red[wave][t][lane * EPL + e];
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) s_red[0][t][lane * EPL + e] = acc[t][e];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t >= nt) break;
+            float o[EPL];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) o[e] = acc[t][e] + s_red[0][t][lane * EPL + e];
+            float *dst = p.partial + ((size_t)sp * p.P + off + t0 + t) * p.H + (size_t)cv * EPL;
+#pragma unroll
+            for (int e = 0; e < EPL; e += 4)
+                *reinterpret_cast<float4 *>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+        }
+    }
+    __syncthreads();  // s_red is rewritten by the next tile
+}
+
+template <class Tr, int TBMAX, int MODE>
 __global__ __launch_bounds__(256) void k_down(DownParams p)
 {
     using V = typename Tr::V;
     constexpr int EPL = Tr::kEpl;
-    constexpr int UR = 4;  // rows per batch per wavefront; two batches in flight
     extern __shared__ uint16_t s_list[];  // the expert's union rows, ascending
-    __shared__ float s_red[2][TB][kWave * EPL];
+    __shared__ float s_red[2][TBMAX][kWave * EPL];
+    __shared__ float s_h[kDownRowChunk * TBMAX];
     __shared__ int s_wpre[4];
 
     const int per_e = p.NCT * p.NSPLIT;
@@ -132,67 +226,26 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
 
     const int lo = (int)(((long long)U * sp) / p.NSPLIT);
     const int hi = (int)(((long long)U * (sp + 1)) / p.NSPLIT);
-    const int mine = hi - lo - wave > 0 ? (hi - lo - wave + 3) / 4 : 0;  // rows of this wavefront
-    const int nb = (mine + UR - 1) / UR;
-
-    for (int t0 = 0; t0 < n; t0 += TB) {
-        const int nt = min(TB, n - t0);
-        float acc[TB][EPL];
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
-
-        // rows lo + wave + 4 i of the split, batches of UR, two in flight
-        DownBatch<Tr, UR, TB> A, B;
-        if (nb > 0) load_down_batch<Tr, UR, TB, MODE>(A, Wd, hb, s_list, lo + wave, hi, n, t0, nt, rowV);
-#pragma unroll 1
-        for (int b = 0; b < nb; b += 2) {
-            if (b + 1 < nb)
-                load_down_batch<Tr, UR, TB, MODE>(B, Wd, hb, s_list, lo + wave + 4 * UR * (b + 1), hi, n, t0, nt, rowV);
-            fma_down_batch<Tr, UR, TB>(A, acc);
-            if (b + 1 >= nb) break;
-            if (b + 2 < nb)
-                load_down_batch<Tr, UR, TB, MODE>(A, Wd, hb, s_list, lo + wave + 4 * UR * (b + 2), hi, n, t0, nt, rowV);
-            fma_down_batch<Tr, UR, TB>(B, acc);
+    // token tiles: the smallest of 1, 2, 4, 8 covering what is left (capped)
+    for (int t0 = 0; t0 < n;) {
+        const int r = n - t0;
+        if (TBMAX >= 8 && r > 4) {
+            down_tile<Tr, (TBMAX >= 8 ? 8 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, min(r, 8),
+                                                             lo, hi, sp, cv, rowV, lane, wave);
+            t0 += 8;
+        } else if (TBMAX >= 4 && r > 2) {
+            down_tile<Tr, (TBMAX >= 4 ? 4 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, min(r, 4),
+                                                             lo, hi, sp, cv, rowV, lane, wave);
+            t0 += 4;
+        } else if (TBMAX >= 2 && r > 1) {
+            down_tile<Tr, (TBMAX >= 2 ? 2 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, 2, lo, hi,
+                                                             sp, cv, rowV, lane, wave);
+            t0 += 2;
+        } else {
+            down_tile<Tr, 1, TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, 1, lo, hi, sp, cv, rowV, lane,
+                                          wave);
+            t0 += 1;
         }
-
-        // wavefront sums in a fixed order: (w0 + w2) + (w1 + w3)
-        if (wave >= 2) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) s_red[wave - 2][t][lane * EPL + e] = acc[t][e];
-        }
-        __syncthreads();
-        if (wave < 2) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[t][e] += s_red[wave][t][lane * EPL + e];
-        }
-        __syncthreads();
-        if (wave == 1) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t)
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) s_red[0][t][lane * EPL + e] = acc[t][e];
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                if (t >= nt) break;
-                float o[EPL];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = acc[t][e] + s_red[0][t][lane * EPL + e];
-                float *dst = p.partial + ((size_t)sp * p.P + off + t0 + t) * p.H + (size_t)cv * EPL;
-#pragma unroll
-                for (int e = 0; e < EPL; e += 4)
-                    *reinterpret_cast<float4 *>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-            }
-        }
-        __syncthreads();  // s_red is rewritten by the next tile
     }
 }
 

@@ -82,8 +82,22 @@ __device__ __forceinline__ void reduce_batch(const typename Tr::V (&buf)[UR][NSW
     if (owner) s_part[wave][slot0 + kidx / TT][kidx % TT] = part;
 }
 
-template <class Tr, int NW, int NSW, int TT, int MODE>
-__global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
+// LDS of one workgroup, sized for the largest token tile.
+template <int NW, int TTMAX>
+struct ProjLds {
+    float part[NW][kChunk][TTMAX];  // per-wavefront partial dots
+    float a[kChunk][TTMAX];         // scores of the tile
+    uint32_t mask[TTMAX];           // mask word per token of the tile
+    uint32_t act;                   // rows active for some token of the tile
+};
+
+// One token tile of TT tokens (nt <= TT valid): gate, scores, masks, up, h.
+// Returns the tile's active-row word.
+template <class Tr, int NW, int NSW, int TT, int TTMAX, int MODE>
+__device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, TTMAX> &L,
+                                              const typename Tr::V *X, const typename Tr::V *Wg,
+                                              const typename Tr::V *Wu, float *hb, int n, int off, int t0,
+                                              int nt, int r0, int c, int Ie, float tau, int lane, int wave)
 {
     using V = typename Tr::V;
     // rows per batch: at most 32 partial sums per reduction and 4 vectors of
@@ -94,15 +108,110 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
     constexpr int M = UR * TT;        // values per reduction
     constexpr int NB = kChunk / UR;   // batches per 32 rows (even)
     static_assert(NB % 2 == 0, "ping-pong needs an even batch count");
+    constexpr int rowV = NW * NSW * kWave;
+    auto &s_part = *reinterpret_cast<float(*)[NW][kChunk][TT]>(&L.part);  // TT-wide view
+    const int kidx = xreduce_index<M>(lane);
+    const bool owner = xreduce_owner<M>(lane);
 
-    __shared__ float s_part[NW][kChunk][TT];  // per-wavefront partial dots
-    __shared__ float s_a[kChunk][TT];         // scores of the tile
-    __shared__ uint32_t s_mask[TT];           // mask word per token of the tile
-    __shared__ uint32_t s_act;                // rows active for some token of the tile
+    // this wavefront's slice of the tile's hidden states
+    V xr[TT][NSW];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int tok = (t < nt) ? p.pair_tok[off + t0 + t] : -1;
+#pragma unroll
+        for (int k = 0; k < NSW; ++k) xr[t][k] = (tok >= 0) ? X[(size_t)tok * rowV + k * kWave] : Tr::zero();
+    }
+    if (threadIdx.x < TT) L.mask[threadIdx.x] = 0u;
+    if (threadIdx.x == 0) L.act = 0u;
 
-    const int nw_per_e = p.C;
-    const int s = blockIdx.x / nw_per_e;
-    const int c = blockIdx.x - s * nw_per_e;
+    // ---- gate: 32 rows in NB batches, two in flight (ping-pong) -------------
+    {
+        V bufA[UR][NSW], bufB[UR][NSW];
+        load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);
+#pragma unroll 1
+        for (int b = 0; b < NB; b += 2) {
+            load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+            if (b + 2 < NB) load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+        }
+    }
+    __syncthreads();
+
+    // ---- scores, masks, active rows -----------------------------------------
+    for (int i = threadIdx.x; i < kChunk * TT; i += NW * kWave) {
+        const int r = i / TT, t = i - r * TT;
+        float g = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) g += s_part[w][r][t];
+        const float a = silu(g);
+        if (MODE == kModeScore) {
+            if (t < nt) hb[(size_t)r * n + t0 + t] = fabsf(a);
+        } else {
+            L.a[r][t] = a;
+            const bool m = (t < nt) && (MODE == MOE_DENSE || !(fabsf(a) < tau));
+            if (m) {
+                atomicOr(&L.mask[t], 1u << r);
+                atomicOr(&L.act, 1u << r);
+            }
+        }
+    }
+    __syncthreads();
+    if (MODE == kModeScore) return 0u;
+    const uint32_t act = __builtin_amdgcn_readfirstlane(L.act);
+    const int nact = __popc(act);
+
+    // ---- up: active rows only, in ascending order ----------------------------
+    if (nact > 0) {
+        const int nbu = (nact + UR - 1) / UR;
+        uint32_t rest = act;  // rows not yet issued (scalar)
+        V bufA[UR][NSW], bufB[UR][NSW];
+        load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+#pragma unroll 1
+        for (int b = 0; b < nbu; b += 2) {
+            if (b + 1 < nbu) load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, rowV);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+            if (b + 1 >= nbu) break;
+            if (b + 2 < nbu) load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+        }
+    }
+    __syncthreads();
+
+    // ---- h for every row of the tile, masks ----------------------------------
+    for (int i = threadIdx.x; i < kChunk * nt; i += NW * kWave) {
+        const int r = i / nt, t = i - r * nt;
+        float hv = 0.f;
+        if ((act >> r) & 1u) {
+            const int slot = __popc(act & ((1u << r) - 1u));  // rank among active rows
+            float u = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) u += s_part[w][slot][t];
+            const bool m = (L.mask[t] >> r) & 1u;
+            hv = m ? L.a[r][t] * u : 0.f;
+        }
+        hb[(size_t)r * n + t0 + t] = hv;
+    }
+    if (p.mask_bits && threadIdx.x < nt) {
+        const int t = threadIdx.x;
+        const int pr = off + t0 + t;
+        const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
+        p.mask_bits[row * p.W + (r0 >> 5)] = L.mask[t];
+        if (c == 0)
+            for (int wd = Ie / 32; wd < p.W; ++wd) p.mask_bits[row * p.W + wd] = 0u;
+    }
+    __syncthreads();  // LDS is rewritten by the next tile
+    return act;
+}
+
+template <class Tr, int NW, int NSW, int TTMAX, int MODE>
+__global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
+{
+    using V = typename Tr::V;
+    __shared__ ProjLds<NW, TTMAX> L;
+
+    const int s = blockIdx.x / p.C;
+    const int c = blockIdx.x - s * p.C;
     if (s >= p.hdr[0]) return;
     const int xe = p.touched[s];
     const bool shared = xe >= p.E;
@@ -123,105 +232,29 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
     float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie)
                 + (size_t)r0 * n;
     const float tau = (MODE == MOE_SPARSE) ? p.tau[xe] : 0.f;
-    const int kidx = xreduce_index<M>(lane);
-    const bool owner = xreduce_owner<M>(lane);
-    uint32_t uni = 0;  // union word of this chunk (thread 0)
 
-    for (int t0 = 0; t0 < n; t0 += TT) {
-        const int nt = min(TT, n - t0);
-        // this wavefront's slice of the tile's hidden states
-        V xr[TT][NSW];
-#pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            const int tok = (t < nt) ? p.pair_tok[off + t0 + t] : -1;
-#pragma unroll
-            for (int k = 0; k < NSW; ++k)
-                xr[t][k] = (tok >= 0) ? X[(size_t)tok * rowV + k * kWave] : Tr::zero();
+    // token tiles: the smallest of 1, 2, 4, 8 covering what is left (capped at
+    // TTMAX), so an expert's rows are streamed once whenever n <= TTMAX
+    uint32_t uni = 0;
+    for (int t0 = 0; t0 < n;) {
+        const int rem = n - t0;
+        if (TTMAX >= 8 && rem > 4) {
+            uni |= proj_tile<Tr, NW, NSW, (TTMAX >= 8 ? 8 : 1), TTMAX, MODE>(
+                p, L, X, Wg, Wu, hb, n, off, t0, min(rem, 8), r0, c, Ie, tau, lane, wave);
+            t0 += 8;
+        } else if (TTMAX >= 4 && rem > 2) {
+            uni |= proj_tile<Tr, NW, NSW, (TTMAX >= 4 ? 4 : 1), TTMAX, MODE>(
+                p, L, X, Wg, Wu, hb, n, off, t0, min(rem, 4), r0, c, Ie, tau, lane, wave);
+            t0 += 4;
+        } else if (TTMAX >= 2 && rem > 1) {
+            uni |= proj_tile<Tr, NW, NSW, (TTMAX >= 2 ? 2 : 1), TTMAX, MODE>(
+                p, L, X, Wg, Wu, hb, n, off, t0, 2, r0, c, Ie, tau, lane, wave);
+            t0 += 2;
+        } else {
+            uni |= proj_tile<Tr, NW, NSW, 1, TTMAX, MODE>(p, L, X, Wg, Wu, hb, n, off, t0, 1, r0, c, Ie, tau,
+                                                          lane, wave);
+            t0 += 1;
         }
-        if (threadIdx.x < TT) s_mask[threadIdx.x] = 0u;
-        if (threadIdx.x == 0) s_act = 0u;
-
-        // ---- gate: 32 rows in NB batches, two in flight (ping-pong) ---------
-        {
-            V bufA[UR][NSW], bufB[UR][NSW];
-            load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);
-#pragma unroll 1
-            for (int b = 0; b < NB; b += 2) {
-                load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
-                reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
-                if (b + 2 < NB) load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
-                reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
-            }
-        }
-        __syncthreads();
-
-        // ---- scores, masks, active rows -------------------------------------
-        for (int i = threadIdx.x; i < kChunk * TT; i += NW * kWave) {
-            const int r = i / TT, t = i - r * TT;
-            float g = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) g += s_part[w][r][t];
-            const float a = silu(g);
-            if (MODE == kModeScore) {
-                if (t < nt) hb[(size_t)r * n + t0 + t] = fabsf(a);
-            } else {
-                s_a[r][t] = a;
-                const bool m = (t < nt) && (MODE == MOE_DENSE || !(fabsf(a) < tau));
-                if (m) {
-                    atomicOr(&s_mask[t], 1u << r);
-                    atomicOr(&s_act, 1u << r);
-                }
-            }
-        }
-        if (MODE == kModeScore) {
-            __syncthreads();  // s_part is rewritten by the next tile
-            continue;
-        }
-        __syncthreads();
-        const uint32_t act = __builtin_amdgcn_readfirstlane(s_act);
-        const int nact = __popc(act);
-
-        // ---- up: active rows only, in ascending order ----------------------
-        if (nact > 0) {
-            const int nbu = (nact + UR - 1) / UR;
-            uint32_t rest = act;  // rows not yet issued (scalar)
-            V bufA[UR][NSW], bufB[UR][NSW];
-            load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
-#pragma unroll 1
-            for (int b = 0; b < nbu; b += 2) {
-                if (b + 1 < nbu) load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, rowV);
-                reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
-                if (b + 1 >= nbu) break;
-                if (b + 2 < nbu) load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
-                reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
-            }
-        }
-        __syncthreads();
-
-        // ---- h for every row of the tile, masks, union ------------------------
-        for (int i = threadIdx.x; i < kChunk * nt; i += NW * kWave) {
-            const int r = i / nt, t = i - r * nt;
-            float hv = 0.f;
-            if ((act >> r) & 1u) {
-                const int slot = __popc(act & ((1u << r) - 1u));  // rank among active rows
-                float u = 0.f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) u += s_part[w][slot][t];
-                const bool m = (s_mask[t] >> r) & 1u;
-                hv = m ? s_a[r][t] * u : 0.f;
-            }
-            hb[(size_t)r * n + t0 + t] = hv;
-        }
-        if (p.mask_bits && threadIdx.x < nt) {
-            const int t = threadIdx.x;
-            const int pr = off + t0 + t;
-            const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
-            p.mask_bits[row * p.W + (r0 >> 5)] = s_mask[t];
-            if (c == 0)
-                for (int wd = Ie / 32; wd < p.W; ++wd) p.mask_bits[row * p.W + wd] = 0u;
-        }
-        uni |= act;
-        __syncthreads();  // LDS is rewritten by the next tile
     }
     if (MODE != kModeScore && threadIdx.x == 0) p.union_words[(size_t)xe * p.W + (r0 >> 5)] = uni;
 }
@@ -240,7 +273,7 @@ static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, int mode, 
 template <class Tr, int NW, int NSW>
 static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
 {
-    switch (pl.TT) {
+    switch (pl.TT) {  // the largest token tile
     case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mode, st);
     case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mode, st);
     case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mode, st);
