@@ -221,9 +221,6 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     float *h = ws_at<float>(ws, pl.off_h);
     float *partial = ws_at<float>(ws, pl.off_partial);
 
-    if (launch_route(a->router_logits, pl.T, pl.E, pl.K, pl.renorm, ids, w, stream) != hipSuccess)
-        return MOE_ERR_HIP;
-
     GroupParams gp{};
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
@@ -234,6 +231,8 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.W = pl.W;
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
+    if (launch_route(a->router_logits, pl.T, pl.E, pl.K, pl.renorm, ids, w, stream) != hipSuccess)
+        return MOE_ERR_HIP;
     if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
@@ -263,8 +262,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     // the events bracket the expert projection (gate, score, mask, up) of both paths
     if (a->prof_event_begin && hipEventRecord((hipEvent_t)a->prof_event_begin, stream) != hipSuccess)
         return MOE_ERR_HIP;
-    if (launch_proj(pl, pp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_proj_mfma(pl, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_proj(pl, pp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
     if (a->prof_event_end && hipEventRecord((hipEvent_t)a->prof_event_end, stream) != hipSuccess)
         return MOE_ERR_HIP;
 
@@ -276,8 +274,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
     dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.NSPLIT = pl.NSPLIT;
     dp.nm = pl.nm;
-    if (launch_down(pl, dp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_down_mfma(pl, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_down(pl, dp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
     cp.partial = partial; cp.topk_w = w; cp.topk_ids = ids; cp.counts = counts; cp.pos = pos; cp.y = a->y;
@@ -337,7 +334,8 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
     pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
     pp.nm = pl.nm;  // INT_MAX: every expert is scored by the GEMV kernel
-    if (launch_proj(pl, pp, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
+    MfmaParams none{};
+    if (launch_proj(pl, pp, none, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
 
     SelectParams sp{};
     sp.scores = scores; sp.counts = counts; sp.offsets = offsets; sp.taus = taus; sp.q = q;

@@ -15,6 +15,9 @@
 // a fixed order; splits land in separate partial buffers that the combine
 // kernel adds in a fixed order, so no floating-point atomics are used and the
 // result is bitwise reproducible.
+#include <type_traits>
+
+#include "mfma_body.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -150,19 +153,26 @@ __device__ __forceinline__ void down_tile(const DownParams &p, float (&s_red)[2]
     __syncthreads();  // s_red is rewritten by the next tile
 }
 
+template <int TBMAX, int EPL>
+struct DownLds {
+    float red[2][TBMAX][kWave * EPL];
+    float h[kDownRowChunk * TBMAX];
+    int wpre[4];
+};
+
+// The GEMV down projection of workgroup `bid`: (expert, column tile, split).
 template <class Tr, int TBMAX, int MODE>
-__global__ __launch_bounds__(256) void k_down(DownParams p)
+__device__ __forceinline__ void down_gemv(const DownParams &p, DownLds<TBMAX, Tr::kEpl> &D, int bid)
 {
     using V = typename Tr::V;
-    constexpr int EPL = Tr::kEpl;
-    extern __shared__ uint16_t s_list[];  // the expert's union rows, ascending
-    __shared__ float s_red[2][TBMAX][kWave * EPL];
-    __shared__ float s_h[kDownRowChunk * TBMAX];
-    __shared__ int s_wpre[4];
+    extern __shared__ uint16_t s_list[];  // the expert's union rows, ascending (dynamic LDS)
+    auto &s_red = D.red;
+    float *s_h = D.h;
+    auto &s_wpre = D.wpre;
 
     const int per_e = p.NCT * p.NSPLIT;
-    const int s = blockIdx.x / per_e;
-    const int rem = blockIdx.x - s * per_e;
+    const int s = bid / per_e;
+    const int rem = bid - s * per_e;
     const int ct = rem / p.NSPLIT;
     const int sp = rem - ct * p.NSPLIT;
     if (s >= p.hdr[0]) return;
@@ -249,33 +259,69 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
     }
 }
 
-template <class Tr, int TB>
-static hipError_t launch_down_t(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+// (256 threads, at least 3 wavefronts per SIMD: 3 workgroups per CU)
+template <class Tr, int TBMAX, int MODE>
+__global__ __launch_bounds__(256, 3) void k_down(DownParams p)
 {
-    const dim3 grid(pl.max_touched * pl.NCT * pl.NSPLIT), block(256);
-    const size_t lds = (size_t)pl.Imax * sizeof(uint16_t);
-    if (mode == MOE_DENSE) hipLaunchKernelGGL((k_down<Tr, TB, MOE_DENSE>), grid, block, 0, st, dp);
-    else hipLaunchKernelGGL((k_down<Tr, TB, MOE_SPARSE>), grid, block, lds, st, dp);
+    __shared__ DownLds<TBMAX, Tr::kEpl> D;
+    down_gemv<Tr, TBMAX, MODE>(p, D, blockIdx.x);
+}
+
+// bf16 layers: one launch runs the GEMV down workgroups [0, gemv_blocks) and
+// the MFMA down tiles (the rest; gemv_blocks is a multiple of 8).
+template <int TBMAX, int MODE>
+__global__ __launch_bounds__(256, 3) void k_down_bf16(DownParams p, MfmaParams mp, int gemv_blocks)
+{
+    __shared__ union {
+        DownLds<TBMAX, BF16::kEpl> gemv;
+        MfmaDownLds mfma;
+    } S;
+    if ((int)blockIdx.x < gemv_blocks) down_gemv<BF16, TBMAX, MODE>(p, S.gemv, blockIdx.x);
+    else mfma_down_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks, gridDim.x - gemv_blocks);
+}
+
+static int round8_down(long long v) { return (int)((v + 7) / 8 * 8); }
+
+template <class Tr, int TB, int MODE>
+static hipError_t launch_down_m(const Plan &pl, const DownParams &dp, const MfmaParams &mp, hipStream_t st)
+{
+    const size_t lds = MODE == MOE_DENSE ? 0 : (size_t)pl.Imax * sizeof(uint16_t);
+    if constexpr (std::is_same<Tr, BF16>::value) {
+        if (pl.use_mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
+            const int gemv = round8_down((long long)pl.max_touched * pl.NCT * pl.NSPLIT);
+            const int grid = gemv + round8_down((long long)pl.max_items * (pl.H / kTC));
+            hipLaunchKernelGGL((k_down_bf16<TB, MODE>), dim3(grid), dim3(256), lds, st, dp, mp, gemv);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_down<Tr, TB, MODE>), dim3(pl.max_touched * pl.NCT * pl.NSPLIT), dim3(256), lds, st, dp);
     return hipGetLastError();
 }
 
+template <class Tr, int TB>
+static hipError_t launch_down_t(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
+{
+    if (mode == MOE_DENSE) return launch_down_m<Tr, TB, MOE_DENSE>(pl, dp, mp, st);
+    return launch_down_m<Tr, TB, MOE_SPARSE>(pl, dp, mp, st);
+}
+
 template <class Tr>
-static hipError_t launch_down_tr(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+static hipError_t launch_down_tr(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
 {
     switch (pl.TT) {
-    case 1: return launch_down_t<Tr, 1>(pl, dp, mode, st);
-    case 2: return launch_down_t<Tr, 2>(pl, dp, mode, st);
-    case 4: return launch_down_t<Tr, 4>(pl, dp, mode, st);
-    case 8: return launch_down_t<Tr, 8>(pl, dp, mode, st);
+    case 1: return launch_down_t<Tr, 1>(pl, dp, mp, mode, st);
+    case 2: return launch_down_t<Tr, 2>(pl, dp, mp, mode, st);
+    case 4: return launch_down_t<Tr, 4>(pl, dp, mp, mode, st);
+    case 8: return launch_down_t<Tr, 8>(pl, dp, mp, mode, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream_t st)
+hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
-    return pl.dtype == MOE_BF16 ? launch_down_tr<BF16>(pl, dp, mode, st)
-                                : launch_down_tr<F32>(pl, dp, mode, st);
+    return pl.dtype == MOE_BF16 ? launch_down_tr<BF16>(pl, dp, mp, mode, st)
+                                : launch_down_tr<F32>(pl, dp, mp, mode, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -141,8 +141,10 @@ hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, in
 hipError_t launch_group(const GroupParams &gp, hipStream_t stream);
 // mode: MOE_SPARSE, MOE_DENSE, or kModeScore (calibration scores)
 constexpr int kModeScore = 2;
-hipError_t launch_proj(const Plan &pl, const ProjParams &pp, int mode, hipStream_t stream);
-hipError_t launch_down(const Plan &pl, const DownParams &dp, int mode, hipStream_t stream);
+// MFMA workgroups (experts with >= nm pairs) run in the same launch for bf16
+// layers with 256-thread GEMV workgroups, else in a second launch.
+hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t stream);
+hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t stream);
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
 hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);

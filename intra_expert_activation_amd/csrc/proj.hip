@@ -24,6 +24,9 @@
 // h goes to a per-expert block [rows][n_e]; rows inactive for every token of
 // the tile get h = 0 without reading w_up.  Mask words and the per-expert
 // union word are written whole, without atomics in global memory.
+#include <type_traits>
+
+#include "mfma_body.h"
 #include "moe_internal.h"
 #include "wave_reduce.h"
 
@@ -204,14 +207,13 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     return act;
 }
 
+// The GEMV projection of workgroup `bid`: one 32-row chunk of one expert.
 template <class Tr, int NW, int NSW, int TTMAX, int MODE>
-__global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
+__device__ __forceinline__ void proj_gemv(const ProjParams &p, ProjLds<NW, TTMAX> &L, int bid)
 {
     using V = typename Tr::V;
-    __shared__ ProjLds<NW, TTMAX> L;
-
-    const int s = blockIdx.x / p.C;
-    const int c = blockIdx.x - s * p.C;
+    const int s = bid / p.C;
+    const int c = bid - s * p.C;
     if (s >= p.hdr[0]) return;
     const int xe = p.touched[s];
     const bool shared = xe >= p.E;
@@ -259,48 +261,93 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
     if (MODE != kModeScore && threadIdx.x == 0) p.union_words[(size_t)xe * p.W + (r0 >> 5)] = uni;
 }
 
-// ---------------------------------------------------------------------------
-template <class Tr, int NW, int NSW, int TT>
-static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
+template <class Tr, int NW, int NSW, int TTMAX, int MODE>
+__global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
 {
-    const dim3 grid(pl.max_touched * pl.C), block(NW * kWave);
-    if (mode == MOE_SPARSE) hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MOE_SPARSE>), grid, block, 0, st, pp);
-    else if (mode == MOE_DENSE) hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MOE_DENSE>), grid, block, 0, st, pp);
-    else hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, kModeScore>), grid, block, 0, st, pp);
-    return hipGetLastError();
+    __shared__ ProjLds<NW, TTMAX> L;
+    proj_gemv<Tr, NW, NSW, TTMAX, MODE>(p, L, blockIdx.x);
+}
+
+// bf16 layers with 256-thread GEMV workgroups: one launch runs the GEMV
+// chunks (workgroups [0, gemv_blocks)) and the MFMA tiles (the rest).
+// gemv_blocks is a multiple of 8, so the MFMA workgroups keep their XCD order.
+template <int NSW, int TTMAX, int MODE>
+__global__ __launch_bounds__(256) void k_proj_bf16(ProjParams p, MfmaParams mp, int gemv_blocks)
+{
+    __shared__ union {
+        ProjLds<4, TTMAX> gemv;
+        MfmaProjLds mfma;
+    } S;
+    if ((int)blockIdx.x < gemv_blocks) {
+        proj_gemv<BF16, 4, NSW, TTMAX, MODE>(p, S.gemv, blockIdx.x);
+    } else {
+        if constexpr (MODE != kModeScore)
+            mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks, gridDim.x - gemv_blocks);
+    }
+}
+
+// ---------------------------------------------------------------------------
+static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
+
+template <class Tr, int NW, int NSW, int TT, int MODE>
+static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, hipStream_t st)
+{
+    const bool mfma = MODE != kModeScore && pl.use_mfma;
+    if constexpr (std::is_same<Tr, BF16>::value && NW == 4) {
+        if (mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
+            const int gemv = round8((long long)pl.max_touched * pl.C);
+            const int grid = gemv + round8((long long)pl.max_items * pl.NT);
+            hipLaunchKernelGGL((k_proj_bf16<NSW, TT, MODE>), dim3(grid), dim3(256), 0, st, pp, mp, gemv);
+            return hipGetLastError();
+        }
+    }
+    {
+        hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MODE>), dim3(pl.max_touched * pl.C), dim3(NW * kWave), 0, st, pp);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !mfma) return e;
+        return launch_proj_mfma(pl, mp, MODE, st);
+    }
+}
+
+template <class Tr, int NW, int NSW, int TT>
+static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
+{
+    if (mode == MOE_SPARSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_SPARSE>(pl, pp, mp, st);
+    if (mode == MOE_DENSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_DENSE>(pl, pp, mp, st);
+    return launch_proj_m<Tr, NW, NSW, TT, kModeScore>(pl, pp, mp, st);
 }
 
 template <class Tr, int NW, int NSW>
-static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
+static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
 {
     switch (pl.TT) {  // the largest token tile
-    case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mode, st);
-    case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mode, st);
-    case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mode, st);
-    case 8: if constexpr (NSW <= 2) return launch_proj_t<Tr, NW, NSW, 8>(pl, pp, mode, st); break;
+    case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mp, mode, st);
+    case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mp, mode, st);
+    case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mp, mode, st);
+    case 8: if constexpr (NSW <= 2) return launch_proj_t<Tr, NW, NSW, 8>(pl, pp, mp, mode, st); break;
     }
     return hipErrorInvalidValue;
 }
 
 template <class Tr>
-static hipError_t launch_proj_tr(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
+static hipError_t launch_proj_tr(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
 {
     // NS 16-byte vectors per lane per row, split over up to 4 wavefronts
     switch (pl.NS) {
-    case 1: return launch_proj_ns<Tr, 1, 1>(pl, pp, mode, st);
-    case 2: return launch_proj_ns<Tr, 2, 1>(pl, pp, mode, st);
-    case 4: return launch_proj_ns<Tr, 4, 1>(pl, pp, mode, st);
-    case 8: return launch_proj_ns<Tr, 4, 2>(pl, pp, mode, st);
-    case 16: return launch_proj_ns<Tr, 4, 4>(pl, pp, mode, st);
+    case 1: return launch_proj_ns<Tr, 1, 1>(pl, pp, mp, mode, st);
+    case 2: return launch_proj_ns<Tr, 2, 1>(pl, pp, mp, mode, st);
+    case 4: return launch_proj_ns<Tr, 4, 1>(pl, pp, mp, mode, st);
+    case 8: return launch_proj_ns<Tr, 4, 2>(pl, pp, mp, mode, st);
+    case 16: return launch_proj_ns<Tr, 4, 4>(pl, pp, mp, mode, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_proj(const Plan &pl, const ProjParams &pp, int mode, hipStream_t st)
+hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
-    return pl.dtype == MOE_BF16 ? launch_proj_tr<BF16>(pl, pp, mode, st)
-                                : launch_proj_tr<F32>(pl, pp, mode, st);
+    return pl.dtype == MOE_BF16 ? launch_proj_tr<BF16>(pl, pp, mp, mode, st)
+                                : launch_proj_tr<F32>(pl, pp, mp, mode, st);
 }
 
 }  // namespace moe

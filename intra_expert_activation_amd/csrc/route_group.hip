@@ -14,13 +14,11 @@ namespace moe {
 // K rounds of a wavefront arg-max pick the experts in descending logit order
 // (ties to the lower id); softmax weights are exp(l - max) / sum exp(l - max).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E,
-                                               int K, int renorm, int32_t *__restrict__ ids,
-                                               float *__restrict__ w)
+// Routes token t with one wavefront.
+__device__ __forceinline__ void route_token(const float *__restrict__ logits, int t, int E, int K, int renorm,
+                                            int32_t *__restrict__ ids, float *__restrict__ w)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-    if (t >= T) return;
     const float *l = logits + (size_t)t * E;
     constexpr int kPer = kMaxExperts / kWave;
     float v[kPer];      // ranking value (NaN ranks as -inf)
@@ -75,6 +73,14 @@ __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits,
     }
 }
 
+__global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E, int K,
+                                               int renorm, int32_t *__restrict__ ids, float *__restrict__ w)
+{
+    const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+    if (t >= T) return;
+    route_token(logits, t, E, K, renorm, ids, w);
+}
+
 hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,
                         float *w, hipStream_t stream)
 {
@@ -111,7 +117,7 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool valid)
     return valid ? m : 0ull;
 }
 
-__global__ __launch_bounds__(1024) void k_group(GroupParams p)
+__device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *ids)
 {
     __shared__ int s_cnt[kGroupWaves][kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_group(GroupParams p)
     for (int base = a_begin; base < a_end; base += kWave) {
         const int a = base + lane;
         const bool valid = a < a_end;
-        const int e = valid ? p.ids[a] : 0;
+        const int e = valid ? ids[a] : 0;
         const uint64_t peers = peers_of(e, valid);
         if (valid && (__ffsll((long long)peers) - 1) == lane) atomicAdd(&s_cnt[wv][e], __popcll(peers));
     }
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(1024) void k_group(GroupParams p)
     for (int base = a_begin; base < a_end; base += kWave) {
         const int a = base + lane;
         const bool valid = a < a_end;
-        const int e = valid ? p.ids[a] : 0;
+        const int e = valid ? ids[a] : 0;
         const uint64_t peers = peers_of(e, valid);
         const int leader = valid ? (__ffsll((long long)peers) - 1) : lane;
         int old = 0;
@@ -266,6 +272,8 @@ __global__ __launch_bounds__(1024) void k_group(GroupParams p)
         p.pos[(size_t)t * p.slots + p.K + s] = pos;
     }
 }
+
+__global__ __launch_bounds__(1024) void k_group(GroupParams p) { group_body(p, p.ids); }
 
 hipError_t launch_group(const GroupParams &gp, hipStream_t stream)
 {
