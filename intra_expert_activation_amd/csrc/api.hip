@@ -73,14 +73,25 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->TT = 1;
     while (p->TT < T && p->TT < tt_cap) p->TT *= 2;
 
-    // down projection: column tiles of 64 lanes x 16 bytes; split the union
-    // rows so the grid has ~1024 workgroups when few experts are touched
-    p->NCT = p->NS;
-    const long long base = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT;
-    long long split = (1024 + base - 1) / base;
-    if (split > 8) split = 8;  // the combine adds NSPLIT partials per (token, slot)
-    if (split < 1) split = 1;
-    p->NSPLIT = (int)split;
+    // down projection: workgroup column tiles of 1024 columns (2 KB of a bf16
+    // row).  Up to GD workgroups (the launcher lowers it to
+    // what the device holds resident at once) each take an equal share of the
+    // (expert tile, column tile, union row) work; a group is cut into at most
+    // KMAX pieces, whose partial sums the combine adds in order.
+    p->NCT = (p->H + 1023) / 1024;
+    {
+        const long long gd = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT * 8;
+        p->GD = (int)(gd < 4096 ? gd : 4096);
+    }
+    // KMAX - 1 >= Imax / kDownChunk, so shares of kDownChunk rows never cut a
+    // group into more than KMAX pieces
+    p->KMAX = 8;
+    if ((p->Imax + kDownChunk - 1) / kDownChunk + 1 > p->KMAX) p->KMAX = (p->Imax + kDownChunk - 1) / kDownChunk + 1;
+    {
+        long long gd = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT * 4;
+        if (gd > 1024) gd = 1024;
+        p->GD = (int)((gd + 7) / 8 * 8);
+    }
 
     // MFMA path: bf16 experts with at least kMfmaMinPairs pairs.  A routed
     // expert has at most T pairs, so with T below the threshold it is off.
@@ -109,12 +120,16 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_counts = take((size_t)p->EX * 4);
     p->off_offsets = take((size_t)(p->EX + 1) * 4);
     p->off_touched = take((size_t)p->EX * 4);
+    p->off_slotn = take((size_t)p->EX * 4);
+    p->off_slotoff = take((size_t)p->EX * 4);
     p->off_pair_tok = take((size_t)p->P * 4);
     p->off_pair_slot = take((size_t)p->P * 4);
     p->off_pos = take((size_t)p->P * 4);
     p->off_union = take((size_t)p->EX * p->W * 4);
+    p->off_ucount = take((size_t)p->EX * 4);
+    p->off_sched = take((size_t)(kSchedHdr + 2 * p->EX) * 4);
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
-    p->off_partial = take(calib ? 0 : (size_t)p->NSPLIT * p->P * p->H * 4);
+    p->off_partial = take(calib ? 0 : (size_t)p->KMAX * p->P * p->H * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
     const size_t blocks = (size_t)p->max_items * p->NT;
     p->off_items = take((size_t)p->max_items * 4);
@@ -214,20 +229,25 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     int32_t *counts = ws_at<int32_t>(ws, pl.off_counts);
     int32_t *offsets = ws_at<int32_t>(ws, pl.off_offsets);
     int32_t *touched = ws_at<int32_t>(ws, pl.off_touched);
+    int32_t *slot_n = ws_at<int32_t>(ws, pl.off_slotn);
+    int32_t *slot_off = ws_at<int32_t>(ws, pl.off_slotoff);
     int32_t *pair_tok = ws_at<int32_t>(ws, pl.off_pair_tok);
     int32_t *pair_slot = ws_at<int32_t>(ws, pl.off_pair_slot);
     int32_t *pos = ws_at<int32_t>(ws, pl.off_pos);
     uint32_t *union_words = ws_at<uint32_t>(ws, pl.off_union);
+    int32_t *ucount = ws_at<int32_t>(ws, pl.off_ucount);
+    int32_t *sched = ws_at<int32_t>(ws, pl.off_sched);
     float *h = ws_at<float>(ws, pl.off_h);
     float *partial = ws_at<float>(ws, pl.off_partial);
 
     GroupParams gp{};
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
-    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
+    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos;
     gp.union_cnt = a->union_cnt;
     gp.union_words = union_words;
+    gp.ucount = ucount;
     gp.W = pl.W;
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
@@ -240,7 +260,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     pp.tau = a->tau;
     pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched;
     pp.pair_tok = pair_tok; pp.pair_slot = pair_slot;
-    pp.h = h; pp.mask_bits = a->mask_bits; pp.union_words = union_words;
+    pp.h = h; pp.mask_bits = a->mask_bits; pp.union_words = union_words; pp.ucount = ucount;
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
     pp.W = pl.W; pp.slots = pl.slots; pp.C = pl.C; pp.R = pl.R;
     pp.nm = pl.nm;
@@ -268,18 +288,19 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
 
     DownParams dp{};
     dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
-    dp.hdr = hdr; dp.counts = counts; dp.offsets = offsets; dp.touched = touched;
-    dp.union_words = union_words; dp.partial = partial;
+    dp.hdr = hdr; dp.counts = counts; dp.offsets = offsets; dp.touched = touched; dp.slot_n = slot_n; dp.slot_off = slot_off;
+    dp.union_words = union_words; dp.ucount = ucount; dp.partial = partial; dp.sched = sched;
     dp.union_idx = a->union_idx; dp.union_cnt = a->union_cnt;
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
-    dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.NSPLIT = pl.NSPLIT;
+    dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.KMAX = pl.KMAX;
     dp.nm = pl.nm;
     if (launch_down(pl, dp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
-    cp.partial = partial; cp.topk_w = w; cp.topk_ids = ids; cp.counts = counts; cp.pos = pos; cp.y = a->y;
-    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.E = pl.E; cp.slots = pl.slots; cp.P = pl.P;
-    cp.NSPLIT = pl.NSPLIT; cp.nm = pl.nm;
+    cp.partial = partial; cp.topk_w = w; cp.topk_ids = ids; cp.counts = counts; cp.offsets = offsets;
+    cp.pos = pos; cp.sched = sched; cp.y = a->y;
+    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.E = pl.E; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT;
+    cp.nm = pl.nm;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -310,6 +331,8 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     int32_t *counts = ws_at<int32_t>(workspace, pl.off_counts);
     int32_t *offsets = ws_at<int32_t>(workspace, pl.off_offsets);
     int32_t *touched = ws_at<int32_t>(workspace, pl.off_touched);
+    int32_t *slot_n = ws_at<int32_t>(workspace, pl.off_slotn);
+    int32_t *slot_off = ws_at<int32_t>(workspace, pl.off_slotoff);
     int32_t *pair_tok = ws_at<int32_t>(workspace, pl.off_pair_tok);
     int32_t *pair_slot = ws_at<int32_t>(workspace, pl.off_pair_slot);
     int32_t *pos = ws_at<int32_t>(workspace, pl.off_pos);
@@ -320,7 +343,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     GroupParams gp{};
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
-    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched;
+    gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr;
     if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;

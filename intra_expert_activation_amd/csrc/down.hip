@@ -6,15 +6,20 @@
 // the down matrix stored neuron-major, an active neuron is one contiguous row
 // of H elements and an inactive one is never read.
 //
-// k_down: one workgroup per (touched expert, column tile, split).  It expands
-// the expert's union bit words into an ascending row list in LDS (popcount
-// prefix), takes its split of that list, and accumulates
+// k_down (GEMV experts, n_e below the MFMA threshold) accumulates
 //     o[pair, cols] += h[row][pair] * w_down[row][cols]
-// for every pair of the expert in register tiles of TB tokens.  The 4
-// wavefronts take interleaved rows of the split and are summed through LDS in
-// a fixed order; splits land in separate partial buffers that the combine
-// kernel adds in a fixed order, so no floating-point atomics are used and the
-// result is bitwise reproducible.
+// over the union rows of each expert.  The work is a sequence of groups, one
+// per (touched expert, token tile of up to 8 of its pairs, 256-column tile),
+// each as long as the expert's union; the sequence is cut into equal
+// contiguous shares of at most kDownChunk rows, one per wavefront (wavefront
+// w of workgroup g takes shares 4g + w, 4g + w + 4 GD, ...).  So an expert
+// with a large union (or many pairs) is spread over several wavefronts
+// instead of setting the kernel's length, and the wavefronts never wait for
+// one another.  A group cut into pieces leaves one partial sum per piece (at
+// most KMAX); the combine kernel adds the pieces and the K slots in a fixed
+// order, so no floating-point atomics are used and the result is bitwise
+// reproducible.  Every workgroup derives the same schedule from the
+// per-expert union sizes; workgroup 0 also stores it for the combine.
 #include <type_traits>
 
 #include "mfma_body.h"
@@ -22,299 +27,524 @@
 
 namespace moe {
 
-constexpr int kDownRowChunk = 256;  // rows of h staged in LDS at a time
+constexpr int kDownTok = 8;      // pairs per token tile (one pass over the rows each)
+constexpr int kMinShare = 32;    // smallest share of a workgroup (union rows)
 
-// Loads of the wavefront's next UR rows: this lane's 16-byte vector of each
-// down row (rows past `hi` read as zero).
-template <class Tr, int UR, int MODE>
-__device__ __forceinline__ void load_down_rows(typename Tr::V (&w)[UR], const typename Tr::V *Wd,
-                                               const uint16_t *list, int i0, int hi, int rowV)
+// A wavefront's lanes own 4 consecutive columns each (8-byte vectors of bf16,
+// 16-byte vectors of fp32), so a wavefront covers 256 columns and the 4
+// wavefronts of a workgroup cover 1024 adjacent columns (2 KB of a bf16 row)
+// and stream the same rows; the groups of an expert's column tiles are
+// adjacent in the schedule, so the rest of each row is read at about the same
+// time by the neighbouring workgroups.  Reading a row's pieces together keeps
+// the DRAM pages open: reading the 512-byte pieces of a row at different times
+// measured 4.7-5.9 TB/s against 6.0-6.4 TB/s for whole rows.
+constexpr int kDownCols = 4 * kWave * 4;  // columns per workgroup column tile
+
+struct DownBF16 {
+    using V = uint2;
+    static constexpr int kEpl = 4;
+    static __device__ __forceinline__ void unpack(V w, float (&f)[4]) {
+        f[0] = __uint_as_float(w.x << 16);
+        f[1] = __uint_as_float(w.x & 0xffff0000u);
+        f[2] = __uint_as_float(w.y << 16);
+        f[3] = __uint_as_float(w.y & 0xffff0000u);
+    }
+};
+template <class Tr> struct DownVec { using type = F32; };
+template <> struct DownVec<BF16> { using type = DownBF16; };
+
+// Orders a wavefront's LDS writes before its own later LDS reads (no
+// workgroup barrier: the list regions are wave-private).
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
 {
 #pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Writes the neuron indices at positions [a, b) of an expert's ascending union
+// list (the set bits of its nw union words; bit i of word w = neuron 32 w + i)
+// to list[0 .. b - a).  Lane l holds words l, l + 64, ...; the neurons are
+// visited 64 at a time (lane i takes neuron 64 kb + i), and a ballot with a
+// masked popcount gives each set bit its position, so the list comes out in
+// ascending order without a per-bit loop.  Stops once position b is reached.
+constexpr int kMaxWordsPerLane = kMaxRows / 32 / kWave;  // 8
+
+// The same for nw <= 64 with lane l's word already loaded.
+__device__ __forceinline__ void wave_union_list_1(uint32_t word, int nw, int a, int b, uint16_t *list, int lane)
+{
+    const uint64_t below = lanemask_lt();
+    int base = 0;
+    for (int kk = 0; 2 * kk < nw && base < b; ++kk) {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)word, 2 * kk);
+        const uint32_t hi = 2 * kk + 1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)word, 2 * kk + 1) : 0u;
+        const bool bit = (((lane < 32) ? lo : hi) >> (lane & 31)) & 1u;
+        const uint64_t m = __ballot(bit);
+        const int pos = base + __popcll(m & below);
+        if (bit && pos >= a && pos < b) list[pos - a] = (uint16_t)(64 * kk + lane);
+        base += __popcll(m);
+    }
+    wave_lds_sync();
+}
+
+__device__ __forceinline__ void wave_union_list(const uint32_t *uw, int nw, int a, int b, uint16_t *list,
+                                                int lane)
+{
+    uint32_t words[kMaxWordsPerLane];
+#pragma unroll
+    for (int r = 0; r < kMaxWordsPerLane; ++r) words[r] = (r * kWave + lane < nw) ? uw[r * kWave + lane] : 0u;
+    const uint64_t below = lanemask_lt();
+    int base = 0;  // union position of the current block's first set bit
+#pragma unroll
+    for (int r = 0; r < kMaxWordsPerLane; ++r) {
+        if (r * kWave >= nw || base >= b) break;
+        for (int kk = 0; kk < kWave / 2; ++kk) {
+            const int w0 = r * kWave + 2 * kk;  // the block's first word
+            if (w0 >= nw || base >= b) break;
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)words[r], 2 * kk);
+            const uint32_t hi = w0 + 1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)words[r], 2 * kk + 1) : 0u;
+            const bool bit = (((lane < 32) ? lo : hi) >> (lane & 31)) & 1u;
+            const uint64_t m = __ballot(bit);
+            const int pos = base + __popcll(m & below);
+            if (bit && pos >= a && pos < b) list[pos - a] = (uint16_t)(w0 * 32 + lane);
+            base += __popcll(m);
+        }
+    }
+    wave_lds_sync();
+}
+
+// One batch of UR rows of a wavefront's list: this lane's vector of each down
+// row, and h[row][token] of the batch spread over NH registers (entry
+// u * TB + t in lane (u * TB + t) % 64 of register (u * TB + t) / 64), so the
+// h values travel with the weights they scale.
+template <class Tr, int TB, int UR>
+struct DownBatch {
+    static constexpr int NH = (UR * TB + kWave - 1) / kWave;
+    typename Tr::V w[UR];
+    float h[NH];    // as loaded; zeroed at use where hok is false
+    bool hok[NH];
+};
+
+template <class Tr, int TB, int UR, int MODE>
+__device__ __forceinline__ void down_issue(DownBatch<Tr, TB, UR> &bt, const typename Tr::V *Wd, int rowV,
+                                           const float *hb, int n, int t0, int nt, const uint16_t *list, int a,
+                                           int L, int i0, int lane)
+{
+    constexpr int NH = DownBatch<Tr, TB, UR>::NH;
+    // Every load is unconditional, from an in-bounds address: entries past L
+    // re-read the list's last row (L >= 1 here) and tokens past nt the last
+    // valid token.  Their h is zeroed, so such a row adds h * w = 0 (weights
+    // are finite); the weights themselves are not masked, since the compiler
+    // would turn that select into a branch around the load, and a load under a
+    // branch makes it wait for every load in flight where the paths join.
+    // h first: it is consumed first, so waiting for it leaves the batch's
+    // weight loads in flight.  Its zeroing happens at use (selecting here would
+    // wait for the load).
+#pragma unroll
+    for (int q = 0; q < NH; ++q) {
+        const int e = q * kWave + lane;
+        const int ih = i0 + e / TB, t = e % TB;
+        const int ihc = min(ih, L - 1);
+        const int jh = (MODE == MOE_DENSE) ? a + ihc : (int)list[ihc];
+        bt.h[q] = hb[(size_t)jh * n + t0 + min(t, nt - 1)];
+        bt.hok[q] = e < UR * TB && ih < L && t < nt;
+    }
+    const int iw = min(i0 + (lane & (UR - 1)), L - 1);
+    const int jw = (MODE == MOE_DENSE) ? a + iw : (int)list[iw];
+    // Wd is the wavefront-uniform start of the column tile: row j's vectors
+    // are Wd + j * rowV + lane
+#pragma unroll
     for (int u = 0; u < UR; ++u) {
-        const int i = i0 + 4 * u;
-        const int j = (i < hi) ? ((MODE == MOE_DENSE) ? i : (int)list[i]) : -1;
-        w[u] = (j >= 0) ? Wd[(size_t)j * rowV] : Tr::zero();
+        const int j = __builtin_amdgcn_readlane(jw, u);
+        bt.w[u] = Wd[(size_t)j * rowV + lane];
     }
 }
 
-// acc[t][:] += h[row][t] * w[row][:] for the batch; h comes from LDS (one
-// broadcast read per 4 tokens), rows past the chunk contribute zero weights.
-template <class Tr, int UR, int TB>
-__device__ __forceinline__ void fma_down_rows(const typename Tr::V (&w)[UR], const float *s_h, int r0,
-                                              float (&acc)[TB][Tr::kEpl])
+// acc[t][:] += h[row][t] * w[row][:] over the batch's rows; h is broadcast
+// from its lane by v_readlane (UR * TB <= 64: one register).
+template <class Tr, int TB, int UR>
+__device__ __forceinline__ void down_fma(const DownBatch<Tr, TB, UR> &bt, float (&acc)[TB][Tr::kEpl])
 {
+    static_assert(UR * TB <= kWave, "one register of h per batch");
+    const float h = bt.hok[0] ? bt.h[0] : 0.f;
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
         float wf[Tr::kEpl];
-        Tr::unpack(w[u], wf);
-        const float *hr = s_h + (size_t)(r0 + 4 * u) * TB;
-        float hv[TB];
+        Tr::unpack(bt.w[u], wf);
 #pragma unroll
-        for (int t = 0; t < TB; t += (TB >= 4 ? 4 : TB)) {
-            if constexpr (TB >= 4) {
-                const float4 q = *reinterpret_cast<const float4 *>(hr + t);
-                hv[t] = q.x; hv[t + 1] = q.y; hv[t + 2] = q.z; hv[t + 3] = q.w;
-            } else {
+        for (int t = 0; t < TB; ++t) {
+            const float hs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), u * TB + t));
 #pragma unroll
-                for (int k = 0; k < TB; ++k) hv[k] = hr[k];
-            }
+            for (int c = 0; c < Tr::kEpl; ++c) acc[t][c] = fmaf(hs, wf[c], acc[t][c]);
         }
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int e = 0; e < Tr::kEpl; ++e) acc[t][e] = fmaf(hv[t], wf[e], acc[t][e]);
     }
 }
 
-// One token tile of TB tokens (nt valid): the split's rows of this column tile.
-// The tile's h values of the split's rows are staged in LDS, kDownRowChunk
-// rows at a time ([row][TB], zero past nt and past the split).
-template <class Tr, int TB, int TBMAX, int MODE>
-__device__ __forceinline__ void down_tile(const DownParams &p, float (&s_red)[2][TBMAX][kWave * Tr::kEpl],
-                                          float *s_h, const uint16_t *s_list, const typename Tr::V *Wd,
-                                          const float *hb, int n, int off, int t0, int nt, int lo, int hi,
-                                          int sp, int cv, int rowV, int lane, int wave)
+// Streams the wavefront's L list rows into acc: batches of UR rows, two in
+// flight.  The steady-state loop always issues the next batch before
+// consuming the current one (no conditional loads inside, so each wait is for
+// exactly one batch); the last one or two batches are peeled.  The scheduling
+// barriers keep each batch's loads ahead of the other batch's arithmetic (left
+// alone, the scheduler sinks the loads below it to shorten live ranges).
+template <class Tr, int TB, int MODE>
+__device__ __forceinline__ void down_stream(const typename Tr::V *Wd, int rowV, const float *hb, int n, int t0,
+                                            int nt, const uint16_t *list, int a, int L, float (&acc)[TB][Tr::kEpl],
+                                            int lane)
 {
-    constexpr int EPL = Tr::kEpl;
-    constexpr int UR = 4;  // rows per batch per wavefront; two batches in flight
+    // rows per batch: 16 registers of weights per batch (two batches in
+    // flight) and one register of h
+    constexpr int UR = sizeof(typename Tr::V) < 16 ? 8 : 4;
+    static_assert(UR * TB <= kWave, "one register of h per batch");
+    const int nb = (L + UR - 1) / UR;
+    if (nb == 0) return;
+    DownBatch<Tr, TB, UR> A, B;
+    down_issue<Tr, TB, UR, MODE>(A, Wd, rowV, hb, n, t0, nt, list, a, L, 0, lane);
+    int k = 0;
+#pragma unroll 1
+    for (; k + 2 < nb; k += 2) {
+        down_issue<Tr, TB, UR, MODE>(B, Wd, rowV, hb, n, t0, nt, list, a, L, (k + 1) * UR, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        down_fma<Tr, TB, UR>(A, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        down_issue<Tr, TB, UR, MODE>(A, Wd, rowV, hb, n, t0, nt, list, a, L, (k + 2) * UR, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        down_fma<Tr, TB, UR>(B, acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k + 1 < nb) {
+        down_issue<Tr, TB, UR, MODE>(B, Wd, rowV, hb, n, t0, nt, list, a, L, (k + 1) * UR, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        down_fma<Tr, TB, UR>(A, acc);
+        down_fma<Tr, TB, UR>(B, acc);
+    } else {
+        down_fma<Tr, TB, UR>(A, acc);
+    }
+}
+
+constexpr int kMaxPieces = 16;  // pieces listed before streaming starts
+
+struct DownPiece {
+    int s, tile, ctg, a, b, k, lofs, pad;
+};
+
+struct DownLds {
+    int start[kMaxExperts];   // exclusive prefix of the work over touched slots
+    int uc[kMaxExperts];      // union size per touched slot (0: not on this path)
+    int xe[kMaxExperts];      // expert of each touched slot
+    int n[kMaxExperts];       // its pair count
+    int off[kMaxExperts];     // its first grouped pair
+    int wsum[4], wmax[4];
+    uint16_t list[4][kDownChunk];             // per wavefront: the pieces' rows
+    DownPiece piece[4][kMaxPieces];           // per wavefront: the pieces
+};
+
+// One piece: union positions [a, b) (at most kDownChunk) of expert xe, token
+// tile `tile`, workgroup column tile ctg, whose rows are list[0 .. b - a).  The
+// wavefront streams its 256 columns of each row and writes them to partial
+// piece k.
+template <class Tr, int TB, int MODE>
+__device__ __forceinline__ void down_piece(const DownParams &p, const uint16_t *list, int xe, int n, int off,
+                                           int tile, int ctg, int a, int b, int k, int lane, int wave)
+{
+    using V = typename Tr::V;
+    constexpr int EPL = Tr::kEpl;                    // 4 columns per lane
+    const int rowV = p.H / EPL;                      // vectors per row
+    const int v0 = ctg * (kDownCols / EPL) + wave * kWave;  // this wavefront's first vector
+    if (v0 >= rowV) return;                          // narrow layers: no columns here
+    const bool shared = xe >= p.E;
+    const int Ie = shared ? p.Is : p.I;
+    const int t0 = tile * kDownTok;
+    const int nt = min(n - t0, kDownTok);
+    const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
+    const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat + v0;
+    const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
+
+
     float acc[TB][EPL];
 #pragma unroll
     for (int t = 0; t < TB; ++t)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[t][e] = 0.f;
+        for (int c = 0; c < EPL; ++c) acc[t][c] = 0.f;
+    down_stream<Tr, TB, MODE>(Wd, rowV, hb, n, t0, nt, list, a, b - a, acc, lane);
 
-    for (int c0 = lo; c0 < hi; c0 += kDownRowChunk) {
-        const int c1 = min(hi, c0 + kDownRowChunk);
-        // stage h[row][t] for rows c0..c1 (padded to a multiple of 4 * UR rows)
-        const int rows = ((c1 - c0 + 4 * UR - 1) / (4 * UR)) * (4 * UR);
-        for (int q = threadIdx.x; q < rows * TB; q += blockDim.x) {
-            const int r = q / TB, t = q - r * TB;
-            const int i = c0 + r;
-            float v = 0.f;
-            if (i < c1 && t < nt) {
-                const int j = (MODE == MOE_DENSE) ? i : (int)s_list[i];
-                v = hb[(size_t)j * n + t0 + t];
-            }
-            s_h[q] = v;
-        }
-        __syncthreads();
-        // rows c0 + wave + 4 i of the chunk, batches of UR, two in flight
-        const int mine = c1 - c0 - wave > 0 ? (c1 - c0 - wave + 3) / 4 : 0;
-        const int nb = (mine + UR - 1) / UR;
-        typename Tr::V A[UR], B[UR];
-        if (nb > 0) load_down_rows<Tr, UR, MODE>(A, Wd, s_list, c0 + wave, c1, rowV);
-#pragma unroll 1
-        for (int b = 0; b < nb; b += 2) {
-            if (b + 1 < nb) load_down_rows<Tr, UR, MODE>(B, Wd, s_list, c0 + wave + 4 * UR * (b + 1), c1, rowV);
-            fma_down_rows<Tr, UR, TB>(A, s_h, wave + 4 * UR * b, acc);
-            if (b + 1 >= nb) break;
-            if (b + 2 < nb) load_down_rows<Tr, UR, MODE>(A, Wd, s_list, c0 + wave + 4 * UR * (b + 2), c1, rowV);
-            fma_down_rows<Tr, UR, TB>(B, s_h, wave + 4 * UR * (b + 1), acc);
-        }
-        __syncthreads();  // s_h is rewritten by the next chunk
-    }
-
-    // wavefront sums in a fixed order: (w0 + w2) + (w1 + w3)
-    if (wave >= 2) {
+    float *dst = p.partial + ((size_t)k * p.P + off + t0) * p.H + (size_t)(v0 + lane) * EPL;
 #pragma unroll
-        for (int t = 0; t < TB; ++t)
+    for (int t = 0; t < TB; ++t)
+        if (t < nt)
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) s_red[wave - 2][t][lane * EPL + e] = acc[t][e];
-    }
-    __syncthreads();
-    if (wave < 2) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[t][e] += s_red[wave][t][lane * EPL + e];
-    }
-    __syncthreads();
-    if (wave == 1) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) s_red[0][t][lane * EPL + e] = acc[t][e];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t >= nt) break;
-            float o[EPL];
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) o[e] = acc[t][e] + s_red[0][t][lane * EPL + e];
-            float *dst = p.partial + ((size_t)sp * p.P + off + t0 + t) * p.H + (size_t)cv * EPL;
-#pragma unroll
-            for (int e = 0; e < EPL; e += 4)
-                *reinterpret_cast<float4 *>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
-        }
-    }
-    __syncthreads();  // s_red is rewritten by the next tile
+            for (int c = 0; c < EPL; c += 4)
+                *reinterpret_cast<float4 *>(dst + (size_t)t * p.H + c) =
+                    make_float4(acc[t][c], acc[t][c + 1], acc[t][c + 2], acc[t][c + 3]);
 }
 
-template <int TBMAX, int EPL>
-struct DownLds {
-    float red[2][TBMAX][kWave * EPL];
-    float h[kDownRowChunk * TBMAX];
-    int wpre[4];
-};
-
-// The GEMV down projection of workgroup `bid`: (expert, column tile, split).
-template <class Tr, int TBMAX, int MODE>
-__device__ __forceinline__ void down_gemv(const DownParams &p, DownLds<TBMAX, Tr::kEpl> &D, int bid)
+// Block-wide exclusive scan of v (one value per thread), with the total and
+// the maximum of m over the workgroup.
+__device__ __forceinline__ int block_excl_scan(DownLds &D, int v, int m, int &total, int &mx, int lane, int wave)
 {
-    using V = typename Tr::V;
-    extern __shared__ uint16_t s_list[];  // the expert's union rows, ascending (dynamic LDS)
-    auto &s_red = D.red;
-    float *s_h = D.h;
-    auto &s_wpre = D.wpre;
-
-    const int per_e = p.NCT * p.NSPLIT;
-    const int s = bid / per_e;
-    const int rem = bid - s * per_e;
-    const int ct = rem / p.NSPLIT;
-    const int sp = rem - ct * p.NSPLIT;
-    if (s >= p.hdr[0]) return;
-    const int xe = p.touched[s];
-    const bool shared = xe >= p.E;
-    const int Ie = shared ? p.Is : p.I;
-    const int n = p.counts[xe];
-    if (n >= p.nm) return;  // this expert takes the MFMA path
-    const int off = p.offsets[xe];
-    const int rowV = p.NCT * kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int cv = ct * kWave + lane;  // this lane's vector of each row
-    const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
-    const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat + cv;
-    const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
-
-    // ---- union row list -----------------------------------------------------
-    int U;
-    if (MODE == MOE_DENSE) {
-        U = Ie;
-    } else {
-        const int nw = Ie / 32;
-        const uint32_t *uw = p.union_words + (size_t)xe * p.W;
-        // popcount prefix over the words: thread i owns words [i*per, i*per+per)
-        const int per = (nw + blockDim.x - 1) / blockDim.x;
-        const int w_begin = threadIdx.x * per;
-        int cnt = 0;
-        for (int i = 0; i < per; ++i)
-            if (w_begin + i < nw) cnt += __popc(uw[w_begin + i]);
-        int incl = cnt;
+    const int incl = wave_incl_scan(v, lane);
+    int wm = m;
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int o = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += o;
-        }
-        if (lane == kWave - 1) s_wpre[wave] = incl;
-        __syncthreads();
-        int wbase = 0;
-        for (int i = 0; i < wave; ++i) wbase += s_wpre[i];
-        U = s_wpre[0] + s_wpre[1] + s_wpre[2] + s_wpre[3];
-        int pos = wbase + incl - cnt;
-        for (int i = 0; i < per; ++i) {
-            const int wd = w_begin + i;
-            if (wd >= nw) break;
-            uint32_t bits = uw[wd];
-            while (bits) {
-                const int b = __ffs(bits) - 1;
-                bits &= bits - 1;
-                s_list[pos++] = (uint16_t)(wd * 32 + b);
+    for (int d = 1; d < kWave; d <<= 1) wm = max(wm, __shfl_xor(wm, d, kWave));
+    if (lane == kWave - 1) D.wsum[wave] = incl;
+    if (lane == 0) D.wmax[wave] = wm;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wave; ++i) base += D.wsum[i];
+    total = D.wsum[0] + D.wsum[1] + D.wsum[2] + D.wsum[3];
+    mx = max(max(D.wmax[0], D.wmax[1]), max(D.wmax[2], D.wmax[3]));
+    __syncthreads();
+    return base + incl - v;
+}
+
+// The GEMV down projection of workgroup g (of p.GD).
+template <class Tr, int MODE>
+__device__ __forceinline__ void down_gemv(const DownParams &p, DownLds &D, int g)
+{
+    using DV = typename DownVec<Tr>::type;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wavefront
+    const int EX = p.E + p.S;
+    const int ntouched = p.hdr[0];
+
+    // ---- schedule: work per touched slot = union size x token tiles ---------
+    // thread i covers slots 2i and 2i + 1 (E + S <= 512)
+    int wl[2], ul[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int s = 2 * threadIdx.x + r;
+        wl[r] = ul[r] = 0;
+        if (s < ntouched) {
+            // slot-ordered experts, pair counts, offsets and union sizes: one
+            // round of independent loads
+            const int xe = p.touched[s];
+            const int n = p.slot_n[s];
+            const int of = p.slot_off[s];
+            const int uc = MODE == MOE_DENSE ? 0 : p.ucount[s];
+            D.xe[s] = xe;
+            D.n[s] = n;
+            D.off[s] = of;
+            if (n < p.nm) {
+                const int U = (MODE == MOE_DENSE) ? (xe >= p.E ? p.Is : p.I) : uc;
+                ul[r] = U;
+                wl[r] = U * ((n + kDownTok - 1) / kDownTok);
+                if (g == 0 && p.union_cnt) p.union_cnt[xe] = U;
             }
         }
-        __syncthreads();
     }
-    if (ct == 0 && sp == 0) {
-        if (p.union_idx)
-            for (int i = threadIdx.x; i < U; i += blockDim.x)
-                p.union_idx[(size_t)xe * p.Imax + i] = (MODE == MOE_DENSE) ? i : (int)s_list[i];
-        if (p.union_cnt && threadIdx.x == 0) p.union_cnt[xe] = U;
+    int total, umax;
+    const int ex = block_excl_scan(D, wl[0] + wl[1], max(ul[0], ul[1]), total, umax, lane, wave);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int s = 2 * threadIdx.x + r;
+        D.start[s] = ex + (r ? wl[0] : 0);
+        D.uc[s] = ul[r];
     }
+    const long long wtot = (long long)p.NCT * total;
+    // GD workgroup shares of at most kDownChunk rows (one list build per
+    // piece), none below kMinShare, and no group cut into more than KMAX
+    // pieces (KMAX - 1 >= Imax / kDownChunk keeps that bound under kDownChunk)
+    long long share = (wtot + p.GD - 1) / p.GD;
+    share = max(share, (long long)kMinShare);
+    share = min(share, (long long)kDownChunk);
+    share = max(share, (long long)((umax + p.KMAX - 2) / (p.KMAX - 1)));
+    if (g == 0) {
+        if (threadIdx.x == 0) p.sched[0] = (int)share;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int s = 2 * threadIdx.x + r;
+            if (s < ntouched) {
+                const int xe = p.touched[s];
+                p.sched[kSchedHdr + xe] = ex + (r ? wl[0] : 0);
+                p.sched[kSchedHdr + EX + xe] = ul[r];
+            }
+        }
+    }
+    __syncthreads();
 
-    const int lo = (int)(((long long)U * sp) / p.NSPLIT);
-    const int hi = (int)(((long long)U * (sp + 1)) / p.NSPLIT);
-    // token tiles: the smallest of 1, 2, 4, 8 covering what is left (capped)
-    for (int t0 = 0; t0 < n;) {
-        const int r = n - t0;
-        if (TBMAX >= 8 && r > 4) {
-            down_tile<Tr, (TBMAX >= 8 ? 8 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, min(r, 8),
-                                                             lo, hi, sp, cv, rowV, lane, wave);
-            t0 += 8;
-        } else if (TBMAX >= 4 && r > 2) {
-            down_tile<Tr, (TBMAX >= 4 ? 4 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, min(r, 4),
-                                                             lo, hi, sp, cv, rowV, lane, wave);
-            t0 += 4;
-        } else if (TBMAX >= 2 && r > 1) {
-            down_tile<Tr, (TBMAX >= 2 ? 2 : 1), TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, 2, lo, hi,
-                                                             sp, cv, rowV, lane, wave);
-            t0 += 2;
-        } else {
-            down_tile<Tr, 1, TBMAX, MODE>(p, s_red, s_h, s_list, Wd, hb, n, off, t0, 1, lo, hi, sp, cv, rowV, lane,
-                                          wave);
-            t0 += 1;
+    // ---- workgroup shares vg = g + j GD: [vg share, (vg + 1) share) ---------
+    // Each round lists up to kMaxPieces pieces (from LDS only), loads all their
+    // union words at once and builds their row lists before any weight is
+    // streamed (and before any store: a load consumed after a store waits for
+    // the store to complete), then streams them.
+    uint16_t *list = D.list[wave];
+    DownPiece *pc = D.piece[wave];
+    const int nwmax = p.Imax / 32;
+    for (long long vg = g; vg * share < wtot; vg += p.GD) {
+        long long pos = vg * share;
+        const long long end = min(pos + share, wtot);
+        while (pos < end) {
+            int np = 0, lofs = 0;
+            while (pos < end && np < kMaxPieces) {
+                // the last slot whose range starts at or before pos (slots with
+                // no work start where the next one does, so they are skipped)
+                int lo = 0, hi = ntouched;  // invariant: NCT * start[lo] <= pos
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) / 2;
+                    if ((long long)p.NCT * D.start[mid] <= pos) lo = mid;
+                    else hi = mid;
+                }
+                const int s = lo;
+                const int U = D.uc[s];
+                const long long sbase = (long long)p.NCT * D.start[s];
+                const int gi = (int)((pos - sbase) / U);  // group within the slot: tile * NCT + ctg
+                const int tile = gi / p.NCT, ctg = gi - tile * p.NCT;
+                const long long gstart = sbase + (long long)gi * U;
+                const int a = (int)(pos - gstart);
+                const int b = (int)(min(end, gstart + U) - gstart);
+                if (lane == 0) pc[np] = DownPiece{s, tile, ctg, a, b, (int)(vg - gstart / share), lofs, 0};
+                ++np;
+                lofs += b - a;
+                pos = gstart + b;
+            }
+            wave_lds_sync();
+            if (MODE != MOE_DENSE) {
+                if (nwmax <= kWave) {
+                    // one union word per lane: every piece's words in flight at once
+                    uint32_t wv[kMaxPieces];
+#pragma unroll
+                    for (int j = 0; j < kMaxPieces; ++j) {
+                        wv[j] = 0u;
+                        if (j < np) {
+                            const int xe = __builtin_amdgcn_readfirstlane(D.xe[pc[j].s]);
+                            const int nw = (xe >= p.E ? p.Is : p.I) / 32;
+                            if (lane < nw) wv[j] = p.union_words[(size_t)xe * p.W + lane];
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < kMaxPieces; ++j)
+                        if (j < np) {
+                            const int xe = __builtin_amdgcn_readfirstlane(D.xe[pc[j].s]);
+                            const int nw = (xe >= p.E ? p.Is : p.I) / 32;
+                            wave_union_list_1(wv[j], nw, __builtin_amdgcn_readfirstlane(pc[j].a),
+                                              __builtin_amdgcn_readfirstlane(pc[j].b),
+                                              list + __builtin_amdgcn_readfirstlane(pc[j].lofs), lane);
+                        }
+                } else {
+                    for (int j = 0; j < np; ++j) {
+                        const int xe = __builtin_amdgcn_readfirstlane(D.xe[pc[j].s]);
+                        const int nw = (xe >= p.E ? p.Is : p.I) / 32;
+                        wave_union_list(p.union_words + (size_t)xe * p.W, nw, __builtin_amdgcn_readfirstlane(pc[j].a),
+                                        __builtin_amdgcn_readfirstlane(pc[j].b),
+                                        list + __builtin_amdgcn_readfirstlane(pc[j].lofs), lane);
+                    }
+                }
+            }
+            for (int j = 0; j < np; ++j) {
+                // uniform piece fields (LDS values are not known to be uniform)
+                const int s = __builtin_amdgcn_readfirstlane(pc[j].s);
+                const int xe = __builtin_amdgcn_readfirstlane(D.xe[s]);
+                const int n = __builtin_amdgcn_readfirstlane(D.n[s]);
+                const int of = __builtin_amdgcn_readfirstlane(D.off[s]);
+                const int tile = __builtin_amdgcn_readfirstlane(pc[j].tile);
+                const int ctg = __builtin_amdgcn_readfirstlane(pc[j].ctg);
+                const int a = __builtin_amdgcn_readfirstlane(pc[j].a);
+                const int b = __builtin_amdgcn_readfirstlane(pc[j].b);
+                const int k = __builtin_amdgcn_readfirstlane(pc[j].k);
+                const int lo = __builtin_amdgcn_readfirstlane(pc[j].lofs);
+                const int nt = min(n - tile * kDownTok, kDownTok);
+                if (nt > 4) down_piece<DV, 8, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
+                else if (nt > 2) down_piece<DV, 4, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
+                else if (nt > 1) down_piece<DV, 2, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
+                else down_piece<DV, 1, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
+            }
+            // the union list output, after the round's streaming
+            if (wave == 0 && p.union_idx)
+                for (int j = 0; j < np; ++j) {
+                    if (__builtin_amdgcn_readfirstlane(pc[j].tile) != 0 || __builtin_amdgcn_readfirstlane(pc[j].ctg) != 0) continue;
+                    const int xe = __builtin_amdgcn_readfirstlane(D.xe[pc[j].s]);
+                    const int a = __builtin_amdgcn_readfirstlane(pc[j].a);
+                    const int b = __builtin_amdgcn_readfirstlane(pc[j].b);
+                    const int lo = __builtin_amdgcn_readfirstlane(pc[j].lofs);
+                    for (int i = lane; i < b - a; i += kWave)
+                        p.union_idx[(size_t)xe * p.Imax + a + i] = (MODE == MOE_DENSE) ? a + i : (int)list[lo + i];
+                }
+            wave_lds_sync();  // the next round rewrites the lists and pieces
         }
     }
 }
 
-// (256 threads, at least 3 wavefronts per SIMD: 3 workgroups per CU)
-template <class Tr, int TBMAX, int MODE>
+// (256 threads, at least 3 wavefronts per SIMD; the launcher sizes GD to the
+// workgroups the device holds at once)
+template <class Tr, int MODE>
 __global__ __launch_bounds__(256, 3) void k_down(DownParams p)
 {
-    __shared__ DownLds<TBMAX, Tr::kEpl> D;
-    down_gemv<Tr, TBMAX, MODE>(p, D, blockIdx.x);
+    __shared__ DownLds D;
+    down_gemv<Tr, MODE>(p, D, blockIdx.x);
 }
 
-// bf16 layers: one launch runs the GEMV down workgroups [0, gemv_blocks) and
-// the MFMA down tiles (the rest; gemv_blocks is a multiple of 8).
-template <int TBMAX, int MODE>
-__global__ __launch_bounds__(256, 3) void k_down_bf16(DownParams p, MfmaParams mp, int gemv_blocks)
+// bf16 layers: one launch runs the GEMV down workgroups [0, GD) and the MFMA
+// down tiles (the rest; GD is a multiple of 8).
+template <int MODE>
+__global__ __launch_bounds__(256, 3) void k_down_bf16(DownParams p, MfmaParams mp)
 {
     __shared__ union {
-        DownLds<TBMAX, BF16::kEpl> gemv;
+        DownLds gemv;
         MfmaDownLds mfma;
     } S;
-    if ((int)blockIdx.x < gemv_blocks) down_gemv<BF16, TBMAX, MODE>(p, S.gemv, blockIdx.x);
-    else mfma_down_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks, gridDim.x - gemv_blocks);
+    if ((int)blockIdx.x < p.GD) down_gemv<BF16, MODE>(p, S.gemv, blockIdx.x);
+    else mfma_down_body<MODE>(mp, S.mfma, blockIdx.x - p.GD, gridDim.x - p.GD);
 }
 
 static int round8_down(long long v) { return (int)((v + 7) / 8 * 8); }
 
-template <class Tr, int TB, int MODE>
-static hipError_t launch_down_m(const Plan &pl, const DownParams &dp, const MfmaParams &mp, hipStream_t st)
+// Workgroups of `kernel` (256 threads) the current device holds at once, per
+// kernel and device (queried once).
+template <class Kernel>
+static int resident_blocks(Kernel kernel)
 {
-    const size_t lds = MODE == MOE_DENSE ? 0 : (size_t)pl.Imax * sizeof(uint16_t);
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+    const int r = per_cu * cus;
+    if (dev < 64) cache[dev] = r;
+    return r;
+}
+
+// GEMV down workgroups: the plan's bound, at most what is resident at once,
+// a multiple of 8 (the MFMA tiles after them keep their XCD order)
+static int down_groups(const Plan &pl, int resident)
+{
+    int gd = pl.GD < resident ? pl.GD : resident;
+    gd = gd / 8 * 8;
+    return gd < 8 ? 8 : gd;
+}
+
+template <class Tr, int MODE>
+static hipError_t launch_down_m(const Plan &pl, const DownParams &dp_in, const MfmaParams &mp, hipStream_t st)
+{
+    DownParams dp = dp_in;
     if constexpr (std::is_same<Tr, BF16>::value) {
         if (pl.use_mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
-            const int gemv = round8_down((long long)pl.max_touched * pl.NCT * pl.NSPLIT);
-            const int grid = gemv + round8_down((long long)pl.max_items * (pl.H / kTC));
-            hipLaunchKernelGGL((k_down_bf16<TB, MODE>), dim3(grid), dim3(256), lds, st, dp, mp, gemv);
+            dp.GD = down_groups(pl, resident_blocks(k_down_bf16<MODE>));
+            const int grid = dp.GD + round8_down((long long)pl.max_items * (pl.H / kTC));
+            hipLaunchKernelGGL((k_down_bf16<MODE>), dim3(grid), dim3(256), 0, st, dp, mp);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((k_down<Tr, TB, MODE>), dim3(pl.max_touched * pl.NCT * pl.NSPLIT), dim3(256), lds, st, dp);
+    dp.GD = down_groups(pl, resident_blocks(k_down<Tr, MODE>));
+    hipLaunchKernelGGL((k_down<Tr, MODE>), dim3(dp.GD), dim3(256), 0, st, dp);
     return hipGetLastError();
-}
-
-template <class Tr, int TB>
-static hipError_t launch_down_t(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
-{
-    if (mode == MOE_DENSE) return launch_down_m<Tr, TB, MOE_DENSE>(pl, dp, mp, st);
-    return launch_down_m<Tr, TB, MOE_SPARSE>(pl, dp, mp, st);
 }
 
 template <class Tr>
 static hipError_t launch_down_tr(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
 {
-    switch (pl.TT) {
-    case 1: return launch_down_t<Tr, 1>(pl, dp, mp, mode, st);
-    case 2: return launch_down_t<Tr, 2>(pl, dp, mp, mode, st);
-    case 4: return launch_down_t<Tr, 4>(pl, dp, mp, mode, st);
-    case 8: return launch_down_t<Tr, 8>(pl, dp, mp, mode, st);
-    }
-    return hipErrorInvalidValue;
+    if (mode == MOE_DENSE) return launch_down_m<Tr, MOE_DENSE>(pl, dp, mp, st);
+    return launch_down_m<Tr, MOE_SPARSE>(pl, dp, mp, st);
 }
 
 hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t st)
@@ -325,41 +555,54 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 }
 
 // ---------------------------------------------------------------------------
-// k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)],
-// with o the sum of the NSPLIT partials (one partial for an expert on the MFMA
-// path).  A workgroup covers one token and 256
-// columns: 64 column quads x 4 thread groups; group g adds the terms
-// (slot, split) with (slot * NSPLIT + split) % 4 == g, and the 4 group sums
-// meet in LDS in a fixed order (so the result is deterministic).
+// k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)].
+// o of a GEMV expert's pair is the sum, in piece order, of the partial sums of
+// the pieces its group (token tile, column tile) was cut into; an MFMA expert
+// writes piece 0 only.  A workgroup covers one token and one 256-column tile:
+// 64 column quads x 4 thread groups; group g adds the slots k with k % 4 == g,
+// and the 4 group sums meet in LDS in a fixed order (so the result is
+// deterministic).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(CombineParams p)
 {
     __shared__ float4 s_acc[3][64];
     const int t = blockIdx.x;
-    const int q = threadIdx.x & 63;  // column quad within the block
-    const int g = threadIdx.x >> 6;  // term group
-    const int c4 = blockIdx.y * 64 + q;
-    const int H4 = p.H / 4;
-    const bool live = c4 < H4;
-    const int nterms = p.slots * p.NSPLIT;
+    const int ct = blockIdx.y;
+    const int q = threadIdx.x & 63;  // column quad within the tile
+    const int g = threadIdx.x >> 6;  // slot group
+    const int c4 = ct * 64 + q;
+    const int EX = p.E + (p.slots - p.K);
+    const long long share = p.sched[0];
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (live) {
-        for (int i = g; i < nterms; i += 4) {
-            const int k = i / p.NSPLIT, sp = i - k * p.NSPLIT;
-            const int e = (k < p.K) ? p.topk_ids[(size_t)t * p.K + k] : p.E + (k - p.K);
-            if (sp > 0 && p.counts[e] >= p.nm) continue;  // MFMA experts write split 0 only
-            const int pr = p.pos[(size_t)t * p.slots + k];
-            const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
-            const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)sp * p.P + pr) * p.H)[c4];
-            y.x = fmaf(wk, v.x, y.x);
-            y.y = fmaf(wk, v.y, y.y);
-            y.z = fmaf(wk, v.z, y.z);
-            y.w = fmaf(wk, v.w, y.w);
+    for (int k = g; k < p.slots; k += 4) {
+        const int e = (k < p.K) ? p.topk_ids[(size_t)t * p.K + k] : p.E + (k - p.K);
+        const int pr = p.pos[(size_t)t * p.slots + k];
+        const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
+        int npieces = 1;
+        if (p.counts[e] < p.nm) {
+            const int U = p.sched[kSchedHdr + EX + e];
+            const int tile = (pr - p.offsets[e]) / kDownTok;
+            const int ctg = c4 / (kDownCols / 4);  // the down kernel's column tile of these columns
+            const long long gstart =
+                (long long)p.NCT * p.sched[kSchedHdr + e] + (long long)(tile * p.NCT + ctg) * U;
+            npieces = U > 0 ? (int)((gstart + U - 1) / share - gstart / share) + 1 : 0;
         }
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int kk = 0; kk < npieces; ++kk) {
+            const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + pr) * p.H)[c4];
+            o.x += v.x;
+            o.y += v.y;
+            o.z += v.z;
+            o.w += v.w;
+        }
+        y.x = fmaf(wk, o.x, y.x);
+        y.y = fmaf(wk, o.y, y.y);
+        y.z = fmaf(wk, o.z, y.z);
+        y.w = fmaf(wk, o.w, y.w);
     }
     if (g > 0) s_acc[g - 1][q] = y;
     __syncthreads();
-    if (g == 0 && live) {
+    if (g == 0) {
         const float4 a = s_acc[0][q], b = s_acc[1][q], c = s_acc[2][q];
         y.x = (y.x + a.x) + (b.x + c.x);
         y.y = (y.y + a.y) + (b.y + c.y);
@@ -372,8 +615,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p)
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
-    const int H4 = pl.H / 4;
-    hipLaunchKernelGGL(k_combine, dim3(pl.T, (H4 + 63) / 64), dim3(256), 0, st, cp);
+    hipLaunchKernelGGL(k_combine, dim3(pl.T, pl.H / 256), dim3(256), 0, st, cp);
     return hipGetLastError();
 }
 

@@ -39,16 +39,17 @@ struct Plan {
     int C;           // row chunks per expert: ceil(Imax / R)
     int TT;          // tokens per register tile
     // down projection kernel
-    int NCT;         // column tiles: H / (64 * epl)
-    int NSPLIT;      // splits of an expert's union rows (deterministic split-K)
+    int NCT;         // down column tiles of 1024 columns: ceil(H / 1024)
+    int KMAX;        // most pieces a down group (expert tile, column tile) is cut into
+    int GD;          // GEMV down workgroups (each takes an equal share of the work)
     // MFMA path for experts with at least `nm` pairs (bf16 only)
     int use_mfma;    // 0 when no expert can reach nm (T < nm) or for fp32 / scores
     int nm;          // pair-count threshold (INT_MAX when the path is off)
     int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
     int max_items;   // upper bound on (expert, 64-token tile) work items
     // workspace layout (byte offsets)
-    size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched;
-    size_t off_pair_tok, off_pair_slot, off_pos, off_union, off_h, off_partial;
+    size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
+    size_t off_pair_tok, off_pair_slot, off_pos, off_union, off_ucount, off_sched, off_h, off_partial;
     size_t off_taus;
     size_t off_items, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
@@ -68,11 +69,14 @@ struct GroupParams {
     int32_t *counts;      // [EX]
     int32_t *offsets;     // [EX+1]
     int32_t *touched;     // [EX], ascending expert ids with count > 0
+    int32_t *slot_n;      // [EX], pair count of touched[s]
+    int32_t *slot_off;    // [EX], first grouped pair of touched[s]
     int32_t *pair_tok;    // [P] token of the pair at each grouped position
     int32_t *pair_slot;   // [P] slot of the pair
     int32_t *pos;         // [T*slots] grouped position of (t, slot)
     int32_t *union_cnt;   // optional output, zeroed for untouched experts
     uint32_t *union_words;// [EX,W], zeroed for the experts on the MFMA path
+    int32_t *ucount;      // [EX] union sizes of the GEMV experts by touched slot, zeroed here
     int W;
     int nm;               // MFMA pair-count threshold
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
@@ -86,30 +90,40 @@ struct ProjParams {
     float *h;             // per-expert blocks [rows][n_e] (fp32)
     uint32_t *mask_bits;  // optional output [T,slots,W]
     uint32_t *union_words;// [EX,W]
+    int32_t *ucount;      // [EX] by touched slot: += popcount of each union word written
     int H, E, I, Is, S, K, A, W, slots, C, R;
     int nm;               // experts with nm or more pairs take the MFMA path
 };
 
+// Down projection schedule, written by GEMV down workgroup 0 and read by the
+// combine: [0] = share (work units per workgroup), [4 + xe] = first work unit
+// of expert xe (in units of its union rows), [4 + EX + xe] = its union size.
+constexpr int kSchedHdr = 4;
+constexpr int kDownChunk = 1024;  // largest share of a down wavefront (union rows)
+
 struct DownParams {
     const void *wd, *swd;
     const float *h;
-    const int32_t *hdr, *counts, *offsets, *touched;
+    const int32_t *hdr, *counts, *offsets, *touched, *slot_n, *slot_off;
     const uint32_t *union_words;
-    float *partial;       // [NSPLIT, P, H]
+    const int32_t *ucount;  // by touched slot
+    float *partial;       // [KMAX, P, H]
+    int32_t *sched;       // [kSchedHdr + 2 EX]
     int32_t *union_idx;   // optional output [EX, Imax]
     int32_t *union_cnt;   // optional output [EX]
-    int H, E, I, Is, S, A, P, W, Imax, NCT, NSPLIT;
+    int H, E, I, Is, S, A, P, W, Imax, NCT, KMAX, GD;
     int nm;
 };
 
 struct CombineParams {
     const float *partial;
     const float *topk_w;
-    const int32_t *topk_ids, *counts;
+    const int32_t *topk_ids, *counts, *offsets;
     const int32_t *pos;
+    const int32_t *sched;
     float *y;
-    int T, H, K, E, slots, P, NSPLIT;
-    int nm;               // MFMA experts write one partial instead of NSPLIT
+    int T, H, K, E, slots, P, NCT;
+    int nm;               // MFMA experts write piece 0 only
 };
 
 struct MfmaParams {

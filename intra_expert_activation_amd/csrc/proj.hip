@@ -258,7 +258,10 @@ __device__ __forceinline__ void proj_gemv(const ProjParams &p, ProjLds<NW, TTMAX
             t0 += 1;
         }
     }
-    if (MODE != kModeScore && threadIdx.x == 0) p.union_words[(size_t)xe * p.W + (r0 >> 5)] = uni;
+    if (MODE != kModeScore && threadIdx.x == 0) {
+        p.union_words[(size_t)xe * p.W + (r0 >> 5)] = uni;
+        atomicAdd(&p.ucount[s], __popc(uni));  // by touched slot; integer: order-independent
+    }
 }
 
 template <class Tr, int NW, int NSW, int TTMAX, int MODE>

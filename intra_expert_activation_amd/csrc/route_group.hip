@@ -186,6 +186,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
                 p.counts[e] = loc[i];
                 p.offsets[e] = run;
                 s_off[e] = run;
+                if (p.ucount) p.ucount[e] = 0;
             }
             run += loc[i];
             ntouched_before += (e < EX && loc[i] > 0) ? 1 : 0;
@@ -206,7 +207,11 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         for (int i = 0; i < kPer; ++i) {
             const int e = lane * kPer + i;
             if (e < EX) {
-                if (loc[i] > 0) p.touched[tpos++] = e;
+                if (loc[i] > 0) {
+                    p.slot_n[tpos] = loc[i];
+                    p.slot_off[tpos] = s_off[e];
+                    p.touched[tpos++] = e;
+                }
                 else if (p.union_cnt) p.union_cnt[e] = 0;
             }
         }
