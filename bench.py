@@ -34,7 +34,17 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 ROTATE = 16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_projection_qwen_decode_T64.json")
-KERNEL_SRC = os.path.join(ROOT, "intra_expert_activation_amd", "csrc", "proj.hip")
+# sources compiled into the expert projection kernel: a stored HBM-traffic
+# measurement is used only while they are unchanged
+KERNEL_SRCS = [os.path.join(ROOT, "intra_expert_activation_amd", "csrc", f)
+               for f in ("proj.hip", "mfma_body.h", "moe_internal.h", "wave_reduce.h")]
+
+
+def kernel_src_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 # name: (config id, default batch, default q, default sweep, description)
@@ -244,8 +254,7 @@ def main():
     traffic = None
     if args.workload == "decode" and T == 64 and os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        src_sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-        if tr.get("kernel_src_sha256") == src_sha:
+        if tr.get("kernel_src_sha256") == kernel_src_sha256():
             traffic = tr.get("hbm_bytes_per_launch")
 
     if T >= 1024:  # prefill: the projection is a dense contraction on MFMA
