@@ -47,17 +47,20 @@ __device__ __forceinline__ void load_rows(typename Tr::V (&buf)[UR][NSW], const 
 }
 
 // Issue the loads of the next UR rows whose bits are set in `rest` (ascending),
-// clearing those bits; missing rows load nothing and read as zero.
+// clearing those bits.  Past the last active row the loads repeat row `last`
+// (the highest active row): every load is unconditional, since a load under a
+// branch makes the compiler wait for all loads in flight where the paths
+// join.  The extra rows' dot products land in slots that are never read.
 template <class Tr, int UR, int NSW>
 __device__ __forceinline__ void load_active_rows(typename Tr::V (&buf)[UR][NSW], const typename Tr::V *W,
-                                                 uint32_t &rest, int rowV)
+                                                 uint32_t &rest, int last, int rowV)
 {
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
-        const int r = rest ? __ffs(rest) - 1 : -1;
+        const int r = rest ? __ffs(rest) - 1 : last;
         rest &= rest - 1;
 #pragma unroll
-        for (int k = 0; k < NSW; ++k) buf[u][k] = (r >= 0) ? W[(size_t)r * rowV + k * kWave] : Tr::zero();
+        for (int k = 0; k < NSW; ++k) buf[u][k] = W[(size_t)r * rowV + k * kWave];
     }
 }
 
@@ -116,28 +119,44 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     const int kidx = xreduce_index<M>(lane);
     const bool owner = xreduce_owner<M>(lane);
 
+    // Two batches in flight (ping-pong).  The steady-state loops always issue
+    // the next batch before reducing the current one, with no conditional
+    // load inside (a load under a branch makes the compiler wait for every
+    // load in flight where the paths join); the last batches are peeled.  The
+    // scheduling barriers keep each batch's loads ahead of the other batch's
+    // arithmetic.
+    V bufA[UR][NSW], bufB[UR][NSW];
+    load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);  // weights first: they do not wait for the tokens
+
     // this wavefront's slice of the tile's hidden states
     V xr[TT][NSW];
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-        const int tok = (t < nt) ? p.pair_tok[off + t0 + t] : -1;
+        const int tok = p.pair_tok[off + t0 + min(t, nt - 1)];  // past nt: a valid token, dots unused
 #pragma unroll
-        for (int k = 0; k < NSW; ++k) xr[t][k] = (tok >= 0) ? X[(size_t)tok * rowV + k * kWave] : Tr::zero();
+        for (int k = 0; k < NSW; ++k) xr[t][k] = X[(size_t)tok * rowV + k * kWave];
     }
     if (threadIdx.x < TT) L.mask[threadIdx.x] = 0u;
     if (threadIdx.x == 0) L.act = 0u;
 
-    // ---- gate: 32 rows in NB batches, two in flight (ping-pong) -------------
+    // ---- gate: 32 rows in NB batches -----------------------------------------
     {
-        V bufA[UR][NSW], bufB[UR][NSW];
-        load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);
+        int b = 0;
 #pragma unroll 1
-        for (int b = 0; b < NB; b += 2) {
+        for (; b + 2 < NB; b += 2) {
             load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+            __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
-            if (b + 2 < NB) load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+            __builtin_amdgcn_sched_barrier(0);
+            load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+            __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+        __builtin_amdgcn_sched_barrier(0);
+        reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+        reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
     }
     __syncthreads();
 
@@ -167,16 +186,28 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     // ---- up: active rows only, in ascending order ----------------------------
     if (nact > 0) {
         const int nbu = (nact + UR - 1) / UR;
+        const int last = 31 - __clz(act);
         uint32_t rest = act;  // rows not yet issued (scalar)
-        V bufA[UR][NSW], bufB[UR][NSW];
-        load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+        load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+        int b = 0;
 #pragma unroll 1
-        for (int b = 0; b < nbu; b += 2) {
-            if (b + 1 < nbu) load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, rowV);
+        for (; b + 2 < nbu; b += 2) {
+            load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+            __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
-            if (b + 1 >= nbu) break;
-            if (b + 2 < nbu) load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, rowV);
+            __builtin_amdgcn_sched_barrier(0);
+            load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+            __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (b + 1 < nbu) {
+            load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+            __builtin_amdgcn_sched_barrier(0);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
+        } else {
+            reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
         }
     }
     __syncthreads();
@@ -275,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
 // chunks (workgroups [0, gemv_blocks)) and the MFMA tiles (the rest).
 // gemv_blocks is a multiple of 8, so the MFMA workgroups keep their XCD order.
 template <int NSW, int TTMAX, int MODE>
-__global__ __launch_bounds__(256) void k_proj_bf16(ProjParams p, MfmaParams mp, int gemv_blocks)
+__global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams mp, int gemv_blocks)
 {
     __shared__ union {
         ProjLds<4, TTMAX> gemv;
