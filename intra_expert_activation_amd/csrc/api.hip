@@ -251,9 +251,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.W = pl.W;
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
-    if (launch_route(a->router_logits, pl.T, pl.E, pl.K, pl.renorm, ids, w, stream) != hipSuccess)
-        return MOE_ERR_HIP;
-    if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_route_group(a->router_logits, pl.renorm, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
     pp.x = a->x; pp.wg = a->w_gate; pp.wu = a->w_up; pp.swg = a->ws_gate; pp.swu = a->ws_up;
@@ -339,14 +337,13 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     float *scores = ws_at<float>(workspace, pl.off_h);
     float *taus = ws_at<float>(workspace, pl.off_taus);
 
-    if (launch_route(logits_calib, pl.T, pl.E, pl.K, 1, ids, w, stream) != hipSuccess) return MOE_ERR_HIP;
     GroupParams gp{};
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr;
-    if (launch_group(gp, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
     pp.x = x_calib; pp.wg = w_gate; pp.wu = w_gate; pp.swg = ws_gate; pp.swu = ws_gate;

@@ -66,7 +66,41 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t *row_base, int k)
 
 // One 64 x 64 x H product C += X[rows sTok] * W[rows given by wrow(r)]^T with the
 // 2x2 wavefront layout; `active` gates the MFMAs of this wavefront (all
-// wavefronts always load, store and synchronise).
+// wavefronts always load, store and synchronise).  Token entries below 0 and
+// rows that wrow() reports as below 0 are padding: they load row 0 of their
+// operand instead (every load is unconditional, so the compiler's waits cover
+// exactly one chunk) and only feed accumulator entries that are never used.
+// K advances in chunks of kKC staged through LDS; two chunks are in flight in
+// registers while the MFMAs consume the one in LDS.
+// Loads of chunk c (this thread's four 16-byte pieces) and their LDS stores.
+#define MOE_GEMM_LOAD(X0, X1, W0, W1, c)                                  \
+    do {                                                                  \
+        X0 = *reinterpret_cast<const uint4 *>(xp0 + (c) * kKC);           \
+        X1 = *reinterpret_cast<const uint4 *>(xp1 + (c) * kKC);           \
+        W0 = *reinterpret_cast<const uint4 *>(wp0 + (c) * kKC);           \
+        W1 = *reinterpret_cast<const uint4 *>(wp1 + (c) * kKC);           \
+    } while (0)
+#define MOE_GEMM_STORE(X0, X1, W0, W1)                                    \
+    do {                                                                  \
+        *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = X0;                  \
+        *reinterpret_cast<uint4 *>(&sX[r + 32][c8 * 8]) = X1;             \
+        *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = W0;                  \
+        *reinterpret_cast<uint4 *>(&sW[r + 32][c8 * 8]) = W1;             \
+    } while (0)
+
+__device__ __forceinline__ void gemm_mma(f32x16_t &acc, uint16_t (*sX)[kRow], uint16_t (*sW)[kRow], int wm, int wn,
+                                         int lane, bool active)
+{
+    if (!active) return;
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s) {
+        const int k = 16 * s + 8 * (lane >> 5);
+        const bf16x8_t a = lds_frag(sX[32 * wm + (lane & 31)], k);
+        const bf16x8_t b = lds_frag(sW[32 * wn + (lane & 31)], k);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+}
+
 template <class WRow>
 __device__ __forceinline__ void gemm_64x64(f32x16_t &acc, uint16_t (*sX)[kRow], uint16_t (*sW)[kRow],
                                            const uint16_t *X, const int *sTok, const uint16_t *W, WRow wrow,
@@ -74,49 +108,53 @@ __device__ __forceinline__ void gemm_64x64(f32x16_t &acc, uint16_t (*sX)[kRow], 
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    uint4 xr[2], wr[2];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int piece = tid + 256 * i, r = piece >> 3, c8 = piece & 7;
-            const int tok = sTok[r];
-            xr[i] = tok >= 0 ? *reinterpret_cast<const uint4 *>(X + (size_t)tok * H + k0 + c8 * 8)
-                             : make_uint4(0, 0, 0, 0);
-            const int row = wrow(r);
-            wr[i] = row >= 0 ? *reinterpret_cast<const uint4 *>(W + (size_t)row * H + k0 + c8 * 8)
-                             : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int piece = tid + 256 * i, r = piece >> 3, c8 = piece & 7;
-            *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = xr[i];
-            *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = wr[i];
-        }
-    };
-    load(0);
-    store();
-    __syncthreads();
-    for (int k0 = 0; k0 < H; k0 += kKC) {
-        const bool more = k0 + kKC < H;
-        if (more) load(k0 + kKC);
-        if (active) {
-#pragma unroll
-            for (int s = 0; s < kKC / 16; ++s) {
-                const int k = 16 * s + 8 * (lane >> 5);
-                const bf16x8_t a = lds_frag(sX[32 * wm + (lane & 31)], k);
-                const bf16x8_t b = lds_frag(sW[32 * wn + (lane & 31)], k);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-            }
-        }
+    // this thread's two 16-byte pieces of each chunk: rows r and r + 32
+    const int r = tid >> 3, c8 = tid & 7;
+    const int t0 = sTok[r], t1 = sTok[r + 32];
+    const int w0 = wrow(r), w1 = wrow(r + 32);
+    const uint16_t *xp0 = X + (size_t)(t0 >= 0 ? t0 : 0) * H + c8 * 8;
+    const uint16_t *xp1 = X + (size_t)(t1 >= 0 ? t1 : 0) * H + c8 * 8;
+    const uint16_t *wp0 = W + (size_t)(w0 >= 0 ? w0 : 0) * H + c8 * 8;
+    const uint16_t *wp1 = W + (size_t)(w1 >= 0 ? w1 : 0) * H + c8 * 8;
+    // chunk c: store it (its loads were issued two chunks earlier), issue chunk
+    // c + 2, multiply, and let every wavefront finish reading LDS before the
+    // next store.  NC = H / kKC is even and at least 8.
+    const int NC = H / kKC;
+    uint4 ax0, ax1, aw0, aw1, bx0, bx1, bw0, bw1;
+    MOE_GEMM_LOAD(ax0, ax1, aw0, aw1, 0);
+    __builtin_amdgcn_sched_barrier(0);  // chunk 0's loads strictly before chunk 1's
+    MOE_GEMM_LOAD(bx0, bx1, bw0, bw1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    int c = 0;
+#pragma unroll 1
+    for (; c + 2 < NC; c += 2) {
+        MOE_GEMM_STORE(ax0, ax1, aw0, aw1);
         __syncthreads();
-        if (more) {
-            store();
-            __syncthreads();
-        }
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_GEMM_LOAD(ax0, ax1, aw0, aw1, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        gemm_mma(acc, sX, sW, wm, wn, lane, active);
+        __syncthreads();
+        MOE_GEMM_STORE(bx0, bx1, bw0, bw1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_GEMM_LOAD(bx0, bx1, bw0, bw1, c + 3);  // c + 2 < NC with c, NC even: c + 3 < NC
+        __builtin_amdgcn_sched_barrier(0);
+        gemm_mma(acc, sX, sW, wm, wn, lane, active);
+        __syncthreads();
     }
+    // c = NC - 2: chunks NC - 2 (a) and NC - 1 (b) are in flight
+    MOE_GEMM_STORE(ax0, ax1, aw0, aw1);
+    __syncthreads();
+    gemm_mma(acc, sX, sW, wm, wn, lane, active);
+    __syncthreads();
+    MOE_GEMM_STORE(bx0, bx1, bw0, bw1);
+    __syncthreads();
+    gemm_mma(acc, sX, sW, wm, wn, lane, active);
+    __syncthreads();
 }
+#undef MOE_GEMM_LOAD
+#undef MOE_GEMM_STORE
 
 struct MfmaProjLds {
     uint16_t sX[kTM][kRow];
@@ -129,13 +167,37 @@ struct MfmaProjLds {
     int sNact;
 };
 
+constexpr int kWdRow = kTC + 32;  // padded LDS row of the down tile (bf16): 320 bytes
+constexpr int kDSeg = 32;         // neuron tiles whose lists are staged at a time
+
 struct MfmaDownLds {
     uint16_t sHhi[kTM][kRow];
     uint16_t sHlo[kTM][kRow];
-    uint16_t sWt[kTC][kRow];  // [column][active row]
-    int sList[kTN];
+    uint16_t sWd[kTN][kWdRow];       // [active row][column], row-major as in memory
+    uint8_t sList[kDSeg][kTN];       // active rows of the segment's neuron tiles
+    int sNact[kDSeg];
     int s_wpre[4];
 };
+
+typedef short bf16x4_bits_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_bits_t lds_bf16x4_t;
+
+// B operand of v_mfma_f32_32x32x16_bf16 from a row-major [k][n] LDS tile
+// (k = neuron, n = column): lane l needs B[8 (l / 32) + j][l % 32], j < 8.
+// ds_read_b64_tr_b16 gives lane i of each 16-lane group element i % 4 of the
+// 8-byte chunk addressed by lane 4 j + i / 4 of the group (measured on gfx950),
+// so lane l = 16 g + i addresses row 8 (g / 2) + i / 4 (+ 4 for j = 4..7),
+// column 16 (g % 2) + 4 (i % 4).  Rows 144 dwords apart put the 32 chunks
+// of a half-wavefront on distinct LDS banks.
+__device__ __forceinline__ bf16x8_t lds_frag_tr(const uint16_t *tile, int ld, int k0, int n0, int lane)
+{
+    const int g = lane >> 4, i = lane & 15;
+    const uint16_t *p0 = tile + (size_t)(k0 + 8 * (g >> 1) + (i >> 2)) * ld + n0 + 16 * (g & 1) + 4 * (i & 3);
+    const bf16x4_bits_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t *)p0);
+    const bf16x4_bits_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4_t *)(p0 + 4 * ld));
+    const bf16x4_bits_t v[2] = {lo, hi};
+    return *reinterpret_cast<const bf16x8_t *>(v);
+}
 
 // Projection of one (item, 64-neuron tile); `b` and `nblocks` are this
 // workgroup's index among the MFMA workgroups and their count (a multiple of 8).
@@ -258,14 +320,22 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
     }
 }
 
-// Down projection of one (item, 128-column tile).
+// Down projection of one (item, 128-column tile): O = sum over the expert's
+// neuron tiles of H_tile[64 tokens x active rows] * W_down[active rows, 128
+// columns], hi and lo halves of H each through the MFMA.  The active rows'
+// down weights are staged row-major (16-byte stores) and read transposed by
+// ds_read_b64_tr_b16; the next active tile's h and weights are loaded while
+// the current one is multiplied.  Loads past the tile's active rows repeat its
+// last active row, and h columns past them are zero: every load is
+// unconditional.
 template <int MODE>
 __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds &S, int b, int nblocks)
 {
     auto &sHhi = S.sHhi;
     auto &sHlo = S.sHlo;
-    auto &sWt = S.sWt;
+    auto &sWd = S.sWd;
     auto &sList = S.sList;
+    auto &sNact = S.sNact;
     auto &s_wpre = S.s_wpre;
 
     const int NCT = p.H / kTC;
@@ -284,48 +354,75 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int NTe = (Ie + kTN - 1) / kTN;
+    // this thread's pieces: h rows tid / 8 and 32 + tid / 8 (16 bytes at
+    // column 8 (tid % 8)); down rows tid / 16 + 16 i (16 bytes at column
+    // 8 (tid % 16)), i < 4
+    const int hr = tid >> 3, hc = (tid & 7) * 8;
+    const int wr = tid >> 4, wc = (tid & 15) * 8;
 
     f32x16_t acc[2] = {};
-    for (int nt = 0; nt < NTe; ++nt) {
-        const int blk = item * p.NT + nt;
-        const int nact = p.nact[blk];
-        if (nact == 0) continue;
-        const int kp = (nact + 15) & ~15;
-        const uint16_t *hhi = p.hhi + (size_t)blk * kTM * kTN;
-        const uint16_t *hlo = p.hlo + (size_t)blk * kTM * kTN;
-        const int pieces_h = kTM * (kp / 8);
-        for (int q = tid; q < pieces_h; q += 256) {
-            const int r = q / (kp / 8), c8 = q - r * (kp / 8);
-            *reinterpret_cast<uint4 *>(&sHhi[r][c8 * 8]) = *reinterpret_cast<const uint4 *>(hhi + r * kTN + c8 * 8);
-            *reinterpret_cast<uint4 *>(&sHlo[r][c8 * 8]) = *reinterpret_cast<const uint4 *>(hlo + r * kTN + c8 * 8);
+    for (int seg = 0; seg < NTe; seg += kDSeg) {
+        const int ns = min(kDSeg, NTe - seg);
+        __syncthreads();  // the previous segment's lists are no longer read
+        for (int q = tid; q < ns * kTN; q += 256) {
+            const int t = q / kTN, c = q - t * kTN;
+            sList[t][c] = p.list[(size_t)(item * p.NT + seg + t) * kTN + c];
         }
-        if (tid < kTN) sList[tid] = tid < nact ? (int)p.list[(size_t)blk * kTN + tid] : 0;
+        if (tid < ns) sNact[tid] = p.nact[item * p.NT + seg + tid];
         __syncthreads();
-        // active down rows, transposed into [column][row]
-        for (int q = tid; q < kp * (kTC / 8); q += 256) {
-            const int c = q / (kTC / 8), c8 = q - c * (kTC / 8);
-            const uint4 v = c < nact ? *reinterpret_cast<const uint4 *>(Wd + (size_t)(nt * kTN + sList[c]) * H + c8 * 8)
-                                     : make_uint4(0, 0, 0, 0);
-            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        // active tiles of the segment, in order
+        auto next_active = [&](int t) {
+            for (; t < ns; ++t)
+                if (sNact[t] > 0) return t;
+            return -1;
+        };
+        int cur = __builtin_amdgcn_readfirstlane(next_active(0));
+        if (cur < 0) continue;
+        uint4 hh0, hh1, hl0, hl1, w0, w1, w2, w3;
+        auto issue = [&](int t) {
+            const int blk = item * p.NT + seg + t;
+            const int na = sNact[t];
+            const uint16_t *hhi = p.hhi + (size_t)blk * kTM * kTN;
+            const uint16_t *hlo = p.hlo + (size_t)blk * kTM * kTN;
+            hh0 = *reinterpret_cast<const uint4 *>(hhi + hr * kTN + hc);
+            hh1 = *reinterpret_cast<const uint4 *>(hhi + (hr + 32) * kTN + hc);
+            hl0 = *reinterpret_cast<const uint4 *>(hlo + hr * kTN + hc);
+            hl1 = *reinterpret_cast<const uint4 *>(hlo + (hr + 32) * kTN + hc);
+            const uint16_t *wt = Wd + (size_t)((seg + t) * kTN) * H + wc;
+            w0 = *reinterpret_cast<const uint4 *>(wt + (size_t)sList[t][min(wr, na - 1)] * H);
+            w1 = *reinterpret_cast<const uint4 *>(wt + (size_t)sList[t][min(wr + 16, na - 1)] * H);
+            w2 = *reinterpret_cast<const uint4 *>(wt + (size_t)sList[t][min(wr + 32, na - 1)] * H);
+            w3 = *reinterpret_cast<const uint4 *>(wt + (size_t)sList[t][min(wr + 48, na - 1)] * H);
+        };
+        issue(cur);
+        while (cur >= 0) {
+            const int kp = (__builtin_amdgcn_readfirstlane(sNact[cur]) + 15) & ~15;
+            *reinterpret_cast<uint4 *>(&sHhi[hr][hc]) = hh0;
+            *reinterpret_cast<uint4 *>(&sHhi[hr + 32][hc]) = hh1;
+            *reinterpret_cast<uint4 *>(&sHlo[hr][hc]) = hl0;
+            *reinterpret_cast<uint4 *>(&sHlo[hr + 32][hc]) = hl1;
+            *reinterpret_cast<uint4 *>(&sWd[wr][wc]) = w0;
+            *reinterpret_cast<uint4 *>(&sWd[wr + 16][wc]) = w1;
+            *reinterpret_cast<uint4 *>(&sWd[wr + 32][wc]) = w2;
+            *reinterpret_cast<uint4 *>(&sWd[wr + 48][wc]) = w3;
+            __syncthreads();
+            const int nxt = __builtin_amdgcn_readfirstlane(next_active(cur + 1));
+            if (nxt >= 0) issue(nxt);
+            __builtin_amdgcn_sched_barrier(0);
+            for (int s = 0; s < kp / 16; ++s) {
+                const int k = 16 * s + 8 * (lane >> 5);
+                const bf16x8_t ahi = lds_frag(sHhi[32 * wm + (lane & 31)], k);
+                const bf16x8_t alo = lds_frag(sHlo[32 * wm + (lane & 31)], k);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sWt[c8 * 8 + 2 * i][c] = (uint16_t)(w4[i] & 0xffffu);
-                sWt[c8 * 8 + 2 * i + 1][c] = (uint16_t)(w4[i] >> 16);
+                for (int nb = 0; nb < 2; ++nb) {
+                    const bf16x8_t bv = lds_frag_tr(&sWd[0][0], kWdRow, 16 * s, 64 * wn + 32 * nb, lane);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, bv, acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, bv, acc[nb], 0, 0, 0);
+                }
             }
+            __syncthreads();
+            cur = nxt;
         }
-        __syncthreads();
-        for (int s = 0; s < kp / 16; ++s) {
-            const int k = 16 * s + 8 * (lane >> 5);
-            const bf16x8_t ahi = lds_frag(sHhi[32 * wm + (lane & 31)], k);
-            const bf16x8_t alo = lds_frag(sHlo[32 * wm + (lane & 31)], k);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const bf16x8_t b = lds_frag(sWt[64 * wn + 32 * nb + (lane & 31)], k);
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, b, acc[nb], 0, 0, 0);
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, b, acc[nb], 0, 0, 0);
-            }
-        }
-        __syncthreads();
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)

@@ -152,7 +152,9 @@ struct SelectParams {
 // ---------------------------------------------------------------------------
 hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,
                         float *w, hipStream_t stream);
-hipError_t launch_group(const GroupParams &gp, hipStream_t stream);
+// Routing then grouping of gp.T tokens (ids/w: the routing outputs, also gp.ids).
+hipError_t launch_route_group(const float *logits, int renorm, int32_t *ids, float *w, const GroupParams &gp,
+                              hipStream_t stream);
 // mode: MOE_SPARSE, MOE_DENSE, or kModeScore (calibration scores)
 constexpr int kModeScore = 2;
 // MFMA workgroups (experts with >= nm pairs) run in the same launch for bf16

@@ -280,8 +280,16 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
 
 __global__ __launch_bounds__(1024) void k_group(GroupParams p) { group_body(p, p.ids); }
 
-hipError_t launch_group(const GroupParams &gp, hipStream_t stream)
+// Routing (many workgroups, one wavefront per token) then grouping (one
+// workgroup).  Routing inside the grouping workgroup measured 36 us at T = 64
+// (16 wavefronts routing tokens one after another), against about 13 us for
+// the two launches.
+hipError_t launch_route_group(const float *logits, int renorm, int32_t *ids, float *w, const GroupParams &gp,
+                              hipStream_t stream)
 {
+    if (gp.T <= 0) return hipSuccess;
+    const hipError_t e = launch_route(logits, gp.T, gp.E, gp.K, renorm, ids, w, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupWaves * kWave), 0, stream, gp);
     return hipGetLastError();
 }
