@@ -9,17 +9,18 @@
 // k_down (GEMV experts, n_e below the MFMA threshold) accumulates
 //     o[pair, cols] += h[row][pair] * w_down[row][cols]
 // over the union rows of each expert.  The work is a sequence of groups, one
-// per (touched expert, token tile of up to 8 of its pairs, 256-column tile),
+// per (touched expert, token tile of up to 8 of its pairs, 1024-column tile),
 // each as long as the expert's union; the sequence is cut into equal
-// contiguous shares of at most kDownChunk rows, one per wavefront (wavefront
-// w of workgroup g takes shares 4g + w, 4g + w + 4 GD, ...).  So an expert
-// with a large union (or many pairs) is spread over several wavefronts
-// instead of setting the kernel's length, and the wavefronts never wait for
-// one another.  A group cut into pieces leaves one partial sum per piece (at
-// most KMAX); the combine kernel adds the pieces and the K slots in a fixed
-// order, so no floating-point atomics are used and the result is bitwise
-// reproducible.  Every workgroup derives the same schedule from the
-// per-expert union sizes; workgroup 0 also stores it for the combine.
+// contiguous shares of at most kDownChunk rows, one per workgroup (workgroup
+// g takes shares g, g + GD, ...; its 4 wavefronts stream the same rows, 256
+// columns each).  So an expert with a large union (or many pairs) is spread
+// over several workgroups instead of setting the kernel's length, and the
+// workgroups never wait for one another.  A group cut into pieces leaves one
+// partial sum per piece (at most KMAX); the combine kernel adds the pieces
+// and the K slots in a fixed order, so no floating-point atomics are used and
+// the result is bitwise reproducible.  Every workgroup derives the same
+// schedule from the per-slot union sizes; workgroup 0 also stores it for the
+// combine.
 #include <type_traits>
 
 #include "mfma_body.h"

@@ -22,8 +22,9 @@
 //               keeps fp32-level accuracy.
 //  k_down_mfma  (item, 128-column tile): O = sum over neuron tiles of
 //               H_tile[64 x active] * W_down[active rows, 128 cols]; the
-//               neuron-major down rows are transposed into LDS (k-contiguous)
-//               for the MFMA B operand.  One output per pair (no split).
+//               neuron-major down rows are staged row-major in LDS and read
+//               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
+//               output per pair (no split).
 // Work indices are remapped so that each XCD (8 per MI355X, each with its own
 // L2) runs a contiguous range: the token tiles of one expert, which read the
 // same weight rows, then share that L2.

@@ -11,7 +11,9 @@ The method: arXiv 2605.08575 as explained on its gist.science page (Technical
 Summary, Methodology: Gate Projection, Activation Masking, Fused Up-Down
 Projection; Results for the target-sparsity calibration).
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -87,55 +89,39 @@ def _textbook(L, x, logits, tau, dense):
 
 
 # --------------------------------------------------------------------------
-# Closed forms derived by hand
+# Closed forms derived by hand (tests/golden/worked_example_h3_e2_i2.json holds
+# the layer, the derivation and the expected values)
 # --------------------------------------------------------------------------
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example_h3_e2_i2.json")))
+
+
 def _worked_layer(renorm, K):
-    """H=3, E=2, I=2.  x = e0, so gate/up values are the first column.
-    Expert 1: g = (ln3, -ln3) -> SiLU = (0.75 ln3, -0.25 ln3); u = (2, 5);
-              down rows (1,-2,0.5) and (7,7,7).
-    Expert 0: g = (ln3, 0)    -> SiLU = (0.75 ln3, 0);        u = (-1, 9);
-              down rows (0,1,0) and (3,3,3).
-    Logits (0, ln3): softmax (1/4, 3/4), so slot 0 is expert 1."""
+    g = GOLDEN["layer"]
     f = np.float32
-    wg = np.array([[[LN3, 0, 0], [0, 0, 0]], [[LN3, 0, 0], [-LN3, 0, 0]]], f)
-    wu = np.array([[[-1, 0, 0], [9, 9, 9]], [[2, 0, 0], [5, 0, 0]]], f)
-    wd = np.array([[[0, 1, 0], [3, 3, 3]], [[1, -2, 0.5], [7, 7, 7]]], f)
-    L = dict(H=3, E=2, I=2, K=K, S=0, I_shared=0, renormalize=renorm, dtype="f32",
-             w_gate=wg, w_up=wu, w_down=wd)
-    x = np.array([[1, 0, 0]], f)
-    logits = np.array([[0, LN3]], f)
+    L = dict(H=g["H"], E=g["E"], I=g["I"], K=K, S=0, I_shared=0, renormalize=renorm, dtype="f32",
+             w_gate=(np.array(g["w_gate_over_ln3"], f) * f(LN3)).astype(f),
+             w_up=np.array(g["w_up"], f), w_down=np.array(g["w_down"], f))
+    x = np.array(g["x"], f)
+    logits = (np.array(g["logits_over_ln3"], f) * f(LN3)).astype(f)
     return L, x, logits
 
 
-@pytest.mark.parametrize("renorm,K,tau,expected", [
-    # top-1 without renormalisation: w = 3/4; expert 1 keeps only neuron 0
-    (0, 1, 0.5, 0.75 * 1.5 * LN3 * np.array([1, -2, 0.5])),
-    # renormalised top-1: w = 1
-    (1, 1, 0.5, 1.5 * LN3 * np.array([1, -2, 0.5])),
-    # tau = 0.25 < 0.25 ln3: the negative-lobe neuron (|a| = 0.2747) is active
-    (1, 1, 0.25, 1.5 * LN3 * np.array([1, -2, 0.5]) - 1.25 * LN3 * np.array([7, 7, 7])),
-    # top-2: 3/4 * expert1 + 1/4 * expert0 (expert 0 neuron 1 has a = 0 < 0.5)
-    (1, 2, 0.5, LN3 * np.array([1.125, -2.4375, 0.5625])),
-])
-def test_worked_example_closed_form(renorm, K, tau, expected):
-    L, x, logits = _worked_layer(renorm, K)
-    r = oracle.moe(L, x, logits, tau)
-    np.testing.assert_allclose(r.y[0], expected, rtol=2e-7, atol=1e-7)
-    assert r.ids[0, 0] == 1
-    m1 = _unpack(r.mask_bits, 2)[0, 0]
-    assert m1.tolist() == ([True, True] if tau == 0.25 else [True, False])
-    if K == 2:
-        assert r.ids[0, 1] == 0
-        assert _unpack(r.mask_bits, 2)[0, 1].tolist() == [True, False]
-        assert r.union_cnt.tolist() == [1, 1]
+@pytest.mark.parametrize("case", GOLDEN["cases"], ids=lambda c: c["note"])
+def test_worked_example_closed_form(case):
+    L, x, logits = _worked_layer(case["renormalize"], case["K"])
+    r = oracle.moe(L, x, logits, case["tau"])
+    np.testing.assert_allclose(r.y[0], LN3 * np.array(case["y_over_ln3"]), rtol=2e-7, atol=1e-7)
+    assert r.ids[0].tolist() == case["ids"]
+    assert _unpack(r.mask_bits, 2)[0].tolist() == case["masks"]
+    if "union_cnt" in case:
+        assert r.union_cnt.tolist() == case["union_cnt"]
 
 
 def test_worked_example_scores_and_equality():
     L, x, logits = _worked_layer(1, 2)
     r = oracle.moe(L, x, logits, 0.0, want_scores=True)
     s = r.scores[0]
-    np.testing.assert_allclose(s[0], [0.75 * LN3, -0.25 * LN3], rtol=1e-7)
-    np.testing.assert_allclose(s[1], [0.75 * LN3, 0.0], rtol=1e-7, atol=0)
+    np.testing.assert_allclose(s, LN3 * np.array(GOLDEN["scores_over_ln3"]), rtol=1e-7, atol=0)
     # tau = 0: a score equal to the threshold (a = 0) counts as active
     assert _unpack(r.mask_bits, 2).all()
 
