@@ -8,7 +8,10 @@ calibrated on the GPU to 85% intra-expert sparsity.  One step is one call of
 moe_sparse_expert_ffn on a batch of T tokens (default 64): routing, grouping,
 dense gate + SiLU + threshold + ballot, gathered up, gathered down, combine.
 Batches rotate over 16 draws so that expert weights are not reused from the
-256 MB Infinity Cache between steps.
+256 MB Infinity Cache between steps.  The timed calls are replayed from a HIP
+graph that holds the calls on all 16 batches in order, as a caller that
+captures a whole forward pass replays them; the time per call with one call
+per graph, and with eager launches, is reported beside it.
 
 Prints ONE JSON line (rank 0) with the headline tokens/s, the roofline of the
 dominant kernel (expert projection: gate, score, mask, up), the speedup over
@@ -147,7 +150,7 @@ def main():
                     topk_ids=torch.empty((Tb, K), dtype=torch.int32, device=dev),
                     topk_w=torch.empty((Tb, K), dtype=torch.float32, device=dev))
 
-    def run(Tb, mode, steps, warmup, kernel_timing, graph):
+    def run(Tb, mode, steps, warmup, kernel_timing, graph, chain=True):
         bs = batches(Tb)
         outs = [make_outputs(Tb) for _ in range(rotate)]
         shape = moe.layer_shape(bs[0][0], Wg, K, renorm, shared[0] if S else None)
@@ -181,7 +184,10 @@ def main():
             call(s % rotate)
         torch.cuda.synchronize()
 
-        graphs = None
+        # graphs: one per batch, and (chain) one holding the calls on all the
+        # batches in order, as a caller that captures a whole forward pass
+        # replays them; a step is still one call on one batch
+        graphs, whole = None, None
         if graph:
             try:
                 graphs = []
@@ -193,18 +199,30 @@ def main():
                         with torch.cuda.graph(g, stream=st):
                             call(r)
                         graphs.append(g)
+                    if chain:
+                        whole = torch.cuda.CUDAGraph()
+                        with torch.cuda.graph(whole, stream=st):
+                            for r in range(rotate):
+                                call(r)
                 torch.cuda.current_stream().wait_stream(st)
                 for r in range(rotate):
                     graphs[r].replay()
+                if whole is not None:
+                    whole.replay()
                 torch.cuda.synchronize()
             except Exception as exc:  # capture unsupported: time eager calls
                 print(f"# graph capture failed ({exc}); timing eager calls", file=sys.stderr)
-                graphs = None
+                graphs, whole = None, None
 
         timers = [moe.Timer() for _ in range(steps)] if kernel_timing else None
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(steps):
+        s = 0
+        if timers is None and whole is not None:
+            while s + rotate <= steps:  # calls s .. s + rotate - 1, batches 0 .. rotate - 1
+                whole.replay()
+                s += rotate
+        while s < steps:
             r = s % rotate
             if timers is not None:
                 call(r, timers[s].events)
@@ -212,12 +230,14 @@ def main():
                 graphs[r].replay()
             else:
                 call(r)
+            s += 1
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
         res = dict(ms_per_step=elapsed * 1e3 / steps, tokens_per_s=Tb * steps / elapsed,
                    call_bytes=float(np.mean(call_bytes)), proj_bytes=float(np.mean(proj_bytes)),
                    proj_flops=float(np.mean(proj_flops)), call_flops=float(np.mean(call_flops)),
-                   union_fraction=active, graph=graphs is not None and timers is None)
+                   union_fraction=active, graph=graphs is not None and timers is None,
+                   calls_per_graph=(rotate if whole is not None and steps >= rotate else 1) if graphs else 0)
         if timers is not None:
             kms = np.array([t.elapsed_ms() for t in timers])
             for t in timers:
@@ -236,6 +256,7 @@ def main():
     # then the whole call timed from graph replays
     head = run(T, moe.MOE_SPARSE, args.steps, args.warmup, kernel_timing=True, graph=False)
     head_g = run(T, moe.MOE_SPARSE, args.steps, args.warmup, kernel_timing=False, graph=use_graph)
+    head_1 = run(T, moe.MOE_SPARSE, args.steps, args.warmup, kernel_timing=False, graph=use_graph, chain=False)
     dense_g = run(T, moe.MOE_DENSE, args.steps, args.warmup, kernel_timing=False, graph=use_graph)
     dense_k = run(T, moe.MOE_DENSE, max(20, args.steps // 4), 5, kernel_timing=True, graph=False)
 
@@ -283,10 +304,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{desc}, T {T}, bf16 weights, tau at q={args.q}",
-                   "global_batch": T, "q": args.q, "timing": "graph replay" if best["graph"] else "eager"},
+                   "global_batch": T, "q": args.q,
+                   "timing": (f"graph replay, {best['calls_per_graph']} calls per graph" if best["graph"]
+                              else "eager")},
         "roofline": roof,
         "speedup_vs_dense": round(dense_g["ms_per_step"] / head_g["ms_per_step"], 3),
         "dense_ms_per_step": round(dense_g["ms_per_step"], 5),
+        "ms_per_step_one_call_per_graph": round(head_1["ms_per_step"], 5),
+        "ms_per_step_eager": round(head["ms_per_step"], 5),
         "dense_proj_frac": round((dense_k["proj_tflops"] / MFMA_PEAK_TFLOPS) if T >= 1024
                                  else (dense_k["proj_gbs"] / HBM_PEAK_GBS), 4),
         "call_hbm_frac": round(head_g["call_gbs"] / HBM_PEAK_GBS, 4),

@@ -79,10 +79,6 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // (expert tile, column tile, union row) work; a group is cut into at most
     // KMAX pieces, whose partial sums the combine adds in order.
     p->NCT = (p->H + 1023) / 1024;
-    {
-        const long long gd = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT * 8;
-        p->GD = (int)(gd < 4096 ? gd : 4096);
-    }
     // KMAX - 1 >= Imax / kDownChunk, so shares of kDownChunk rows never cut a
     // group into more than KMAX pieces
     p->KMAX = 8;

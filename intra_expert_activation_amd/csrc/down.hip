@@ -564,9 +564,11 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 // and the 4 group sums meet in LDS in a fixed order (so the result is
 // deterministic).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_combine(CombineParams p)
+// NB: slots per thread group whose loads are issued together (1, 2 or 4).
+template <int NB>
+__device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_acc)[3][64])
 {
-    __shared__ float4 s_acc[3][64];
+    constexpr int kCombBatch = NB;
     const int t = blockIdx.x;
     const int ct = blockIdx.y;
     const int q = threadIdx.x & 63;  // column quad within the tile
@@ -574,32 +576,57 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p)
     const int c4 = ct * 64 + q;
     const int EX = p.E + (p.slots - p.K);
     const long long share = p.sched[0];
+    const int ctg = c4 / (kDownCols / 4);  // the down kernel's column tile of these columns
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = g; k < p.slots; k += 4) {
-        const int e = (k < p.K) ? p.topk_ids[(size_t)t * p.K + k] : p.E + (k - p.K);
-        const int pr = p.pos[(size_t)t * p.slots + k];
-        const float wk = (k < p.K) ? p.topk_w[(size_t)t * p.K + k] : 1.f;
-        int npieces = 1;
-        if (p.counts[e] < p.nm) {
-            const int U = p.sched[kSchedHdr + EX + e];
-            const int tile = (pr - p.offsets[e]) / kDownTok;
-            const int ctg = c4 / (kDownCols / 4);  // the down kernel's column tile of these columns
-            const long long gstart =
-                (long long)p.NCT * p.sched[kSchedHdr + e] + (long long)(tile * p.NCT + ctg) * U;
-            npieces = U > 0 ? (int)((gstart + U - 1) / share - gstart / share) + 1 : 0;
+    // slots k = g, g + 4, ... in batches of kCombBatch: each batch's metadata,
+    // then its partial sums, are loaded as independent loads (a few memory
+    // latencies per batch instead of a chain per slot)
+    for (int k0 = g; k0 < p.slots; k0 += 4 * kCombBatch) {
+        int e[kCombBatch], pr[kCombBatch], np[kCombBatch];
+        float wk[kCombBatch];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j) {
+            const int k = min(k0 + 4 * j, p.slots - 1);
+            const int rid = p.topk_ids[(size_t)t * p.K + min(k, p.K - 1)];
+            const float rw = p.topk_w[(size_t)t * p.K + min(k, p.K - 1)];
+            e[j] = (k < p.K) ? rid : p.E + (k - p.K);
+            wk[j] = (k < p.K) ? rw : 1.f;
+            pr[j] = p.pos[(size_t)t * p.slots + k];
         }
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int kk = 0; kk < npieces; ++kk) {
-            const float4 v = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + pr) * p.H)[c4];
-            o.x += v.x;
-            o.y += v.y;
-            o.z += v.z;
-            o.w += v.w;
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j) {
+            const int cnt = p.counts[e[j]];
+            const int U = p.sched[kSchedHdr + EX + e[j]];
+            const int st = p.sched[kSchedHdr + e[j]];
+            const int of = p.offsets[e[j]];
+            int n = 1;  // an MFMA expert writes piece 0 only
+            if (cnt < p.nm) {
+                const int tile = (pr[j] - of) / kDownTok;
+                const long long gstart = (long long)p.NCT * st + (long long)(tile * p.NCT + ctg) * U;
+                n = U > 0 ? (int)((gstart + U - 1) / share - gstart / share) + 1 : 0;
+            }
+            np[j] = n;
         }
-        y.x = fmaf(wk, o.x, y.x);
-        y.y = fmaf(wk, o.y, y.y);
-        y.z = fmaf(wk, o.z, y.z);
-        y.w = fmaf(wk, o.w, y.w);
+        float4 o[kCombBatch];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j)
+            o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)pr[j] * p.H)[c4];
+#pragma unroll
+        for (int j = 0; j < kCombBatch; ++j) {
+            if (k0 + 4 * j >= p.slots) break;
+            float4 v = np[j] > 0 ? o[j] : make_float4(0.f, 0.f, 0.f, 0.f);  // no piece: o = 0
+            for (int kk = 1; kk < np[j]; ++kk) {
+                const float4 w = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + pr[j]) * p.H)[c4];
+                v.x += w.x;
+                v.y += w.y;
+                v.z += w.z;
+                v.w += w.w;
+            }
+            y.x = fmaf(wk[j], v.x, y.x);
+            y.y = fmaf(wk[j], v.y, y.y);
+            y.z = fmaf(wk[j], v.z, y.z);
+            y.w = fmaf(wk[j], v.w, y.w);
+        }
     }
     if (g > 0) s_acc[g - 1][q] = y;
     __syncthreads();
@@ -611,6 +638,14 @@ __global__ __launch_bounds__(256) void k_combine(CombineParams p)
         y.w = (y.w + a.w) + (b.w + c.w);
         reinterpret_cast<float4 *>(p.y + (size_t)t * p.H)[c4] = y;
     }
+}
+
+__global__ __launch_bounds__(256) void k_combine(CombineParams p)
+{
+    __shared__ float4 s_acc[3][64];
+    if (p.slots <= 4) combine_body<1>(p, s_acc);
+    else if (p.slots <= 8) combine_body<2>(p, s_acc);
+    else combine_body<4>(p, s_acc);
 }
 
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t st)

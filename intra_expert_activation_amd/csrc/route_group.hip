@@ -14,6 +14,16 @@ namespace moe {
 // K rounds of a wavefront arg-max pick the experts in descending logit order
 // (ties to the lower id); softmax weights are exp(l - max) / sum exp(l - max).
 // ---------------------------------------------------------------------------
+// Weight of a chosen expert with exp value ev: its softmax probability
+// ev / denom, or renormalised over the K chosen, ev / sel_sum (the same
+// quotient of probabilities with denom cancelled).  A NaN denominator (a NaN
+// or +inf logit) makes every probability NaN, and so every weight.
+__device__ __forceinline__ float slot_weight(float ev, float sel_sum, float denom, int renorm)
+{
+    if (!renorm) return ev / denom;
+    return isnan(denom) ? denom : ev / sel_sum;
+}
+
 // Routes token t with one wavefront.
 __device__ __forceinline__ void route_token(const float *__restrict__ logits, int t, int E, int K, int renorm,
                                             int32_t *__restrict__ ids, float *__restrict__ w)
@@ -67,10 +77,7 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
         sel_sum += ev;
         if (lane == 0) ids[(size_t)t * K + k] = win;
     }
-    if (lane < K) {
-        const float p = chosen_e / denom;
-        w[(size_t)t * K + lane] = renorm ? chosen_e / sel_sum : p;
-    }
+    if (lane < K) w[(size_t)t * K + lane] = slot_weight(chosen_e, sel_sum, denom, renorm);
 }
 
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E, int K,
@@ -117,6 +124,16 @@ __device__ __forceinline__ uint64_t peers_of(int e, bool valid)
     return valid ? m : 0ull;
 }
 
+constexpr int kIdBatch = 8;
+
+// The ids of chunks b0, b0 + 64, ... (kIdBatch of them) for this lane; loads
+// past a_end repeat the last id (unconditional loads, never used).
+__device__ __forceinline__ void load_id_batch(const int32_t *ids, int b0, int a_end, int lane, int (&ev)[kIdBatch])
+{
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) ev[j] = ids[min(b0 + j * kWave + lane, a_end - 1)];
+}
+
 __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *ids)
 {
     __shared__ int s_cnt[kGroupWaves][kMaxExperts];
@@ -134,13 +151,20 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     const int a_begin = wv * per_wave * kWave;
     const int a_end = min(p.A, (wv + 1) * per_wave * kWave);
 
-    // pass 1: per-wavefront counts
-    for (int base = a_begin; base < a_end; base += kWave) {
-        const int a = base + lane;
-        const bool valid = a < a_end;
-        const int e = valid ? ids[a] : 0;
-        const uint64_t peers = peers_of(e, valid);
-        if (valid && (__ffsll((long long)peers) - 1) == lane) atomicAdd(&s_cnt[wv][e], __popcll(peers));
+    // pass 1: per-wavefront counts (the ids of kIdBatch chunks are loaded at
+    // once: one memory latency per batch instead of one per chunk)
+    for (int b0 = a_begin; b0 < a_end; b0 += kIdBatch * kWave) {
+        int ev[kIdBatch];
+        load_id_batch(ids, b0, a_end, lane, ev);
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) {
+            const int base = b0 + j * kWave;
+            if (base >= a_end) break;
+            const bool valid = base + lane < a_end;
+            const int e = valid ? ev[j] : 0;
+            const uint64_t peers = peers_of(e, valid);
+            if (valid && (__ffsll((long long)peers) - 1) == lane) atomicAdd(&s_cnt[wv][e], __popcll(peers));
+        }
     }
     __syncthreads();
 
@@ -250,22 +274,29 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         }
 
     // pass 2: stable scatter of the routed pairs
-    for (int base = a_begin; base < a_end; base += kWave) {
-        const int a = base + lane;
-        const bool valid = a < a_end;
-        const int e = valid ? ids[a] : 0;
-        const uint64_t peers = peers_of(e, valid);
-        const int leader = valid ? (__ffsll((long long)peers) - 1) : lane;
-        int old = 0;
-        if (valid && leader == lane) old = atomicAdd(&s_cnt[wv][e], __popcll(peers));
-        old = __shfl(old, leader, kWave);
-        if (valid) {
-            const int rank = __popcll(peers & lanemask_lt());
-            const int pos = s_off[e] + old + rank;
-            const int t = a / p.K, k = a - t * p.K;
-            p.pair_tok[pos] = t;
-            p.pair_slot[pos] = k;
-            p.pos[(size_t)t * p.slots + k] = pos;
+    for (int b0 = a_begin; b0 < a_end; b0 += kIdBatch * kWave) {
+        int ev[kIdBatch];
+        load_id_batch(ids, b0, a_end, lane, ev);
+#pragma unroll
+        for (int j = 0; j < kIdBatch; ++j) {
+            const int base = b0 + j * kWave;
+            if (base >= a_end) break;
+            const int a = base + lane;
+            const bool valid = a < a_end;
+            const int e = valid ? ev[j] : 0;
+            const uint64_t peers = peers_of(e, valid);
+            const int leader = valid ? (__ffsll((long long)peers) - 1) : lane;
+            int old = 0;
+            if (valid && leader == lane) old = atomicAdd(&s_cnt[wv][e], __popcll(peers));
+            old = __shfl(old, leader, kWave);
+            if (valid) {
+                const int rank = __popcll(peers & lanemask_lt());
+                const int pos = s_off[e] + old + rank;
+                const int t = a / p.K, k = a - t * p.K;
+                p.pair_tok[pos] = t;
+                p.pair_slot[pos] = k;
+                p.pos[(size_t)t * p.slots + k] = pos;
+            }
         }
     }
     // shared experts: pair A + s*T + t
@@ -281,9 +312,10 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
 __global__ __launch_bounds__(1024) void k_group(GroupParams p) { group_body(p, p.ids); }
 
 // Routing (many workgroups, one wavefront per token) then grouping (one
-// workgroup).  Routing inside the grouping workgroup measured 36 us at T = 64
-// (16 wavefronts routing tokens one after another), against about 13 us for
-// the two launches.
+// workgroup).  Routing inside the grouping workgroup was slower at every
+// batch size measured (1 to 64 tokens, with 1 to 64 lanes per token): one
+// compute unit routes the batch, and the grouping alone costs about as much
+// as the second launch saves.
 hipError_t launch_route_group(const float *logits, int renorm, int32_t *ids, float *w, const GroupParams &gp,
                               hipStream_t stream)
 {

@@ -249,6 +249,27 @@ def test_route_topk(T, E, K, renorm):
     np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=2e-6, atol=1e-8)
 
 
+# Routing inside the layer call, for E from 3 to 512 and K up to 32.  Ties go
+# to the lower id; a NaN logit ranks last and makes its token's softmax
+# denominator, so every weight of that token, NaN (renormalised or not).
+@pytest.mark.parametrize("T,E,K,renorm", [(1, 8, 2, 1), (9, 3, 3, 0), (64, 16, 4, 1), (40, 32, 8, 1),
+                                          (64, 64, 6, 0), (64, 128, 8, 1), (256, 128, 8, 1), (20, 256, 32, 1),
+                                          (7, 512, 32, 0), (300, 128, 8, 1), (1500, 8, 2, 1)])
+def test_layer_routing(T, E, K, renorm):
+    c, L = cached_layer(2, (("H", 512), ("E", E), ("K", K), ("I", 64), ("renormalize", renorm)))
+    DL = layer_to_device(L)
+    rng = np.random.default_rng([T, E, K, 7])
+    x, _ = synth.make_tokens(c, 2, T)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[: (T + 1) // 2, 1] = logits[: (T + 1) // 2, 0]  # ties: the lower id first
+    if E > 2:
+        logits[T - 1, 2] = np.nan
+    out = gpu_ffn(DL, x, logits, 0.0)
+    oids, ow = oracle.route(logits, K, renorm)
+    np.testing.assert_array_equal(out["topk_ids"], oids)
+    np.testing.assert_allclose(out["topk_w"], ow, rtol=2e-6, atol=1e-8, equal_nan=True)
+
+
 # ---------------------------------------------------------------------------
 # Calibration on the GPU
 # ---------------------------------------------------------------------------
