@@ -120,10 +120,9 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_slotoff = take((size_t)p->EX * 4);
     p->off_pair_tok = take((size_t)p->P * 4);
     p->off_pair_slot = take((size_t)p->P * 4);
-    p->off_pos = take((size_t)p->P * 4);
     p->off_union = take((size_t)p->EX * p->W * 4);
     p->off_ucount = take((size_t)p->EX * 4);
-    p->off_sched = take((size_t)(kSchedHdr + 2 * p->EX) * 4);
+    p->off_npc = take(calib ? 0 : (size_t)p->P * p->NCT * 4);
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
     p->off_partial = take(calib ? 0 : (size_t)p->KMAX * p->P * p->H * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
@@ -229,10 +228,9 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     int32_t *slot_off = ws_at<int32_t>(ws, pl.off_slotoff);
     int32_t *pair_tok = ws_at<int32_t>(ws, pl.off_pair_tok);
     int32_t *pair_slot = ws_at<int32_t>(ws, pl.off_pair_slot);
-    int32_t *pos = ws_at<int32_t>(ws, pl.off_pos);
     uint32_t *union_words = ws_at<uint32_t>(ws, pl.off_union);
     int32_t *ucount = ws_at<int32_t>(ws, pl.off_ucount);
-    int32_t *sched = ws_at<int32_t>(ws, pl.off_sched);
+    int32_t *npc = ws_at<int32_t>(ws, pl.off_npc);
     float *h = ws_at<float>(ws, pl.off_h);
     float *partial = ws_at<float>(ws, pl.off_partial);
 
@@ -240,7 +238,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
-    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos;
+    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot;
     gp.union_cnt = a->union_cnt;
     gp.union_words = union_words;
     gp.ucount = ucount;
@@ -268,7 +266,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     mp.pair_tok = pair_tok; mp.pair_slot = pair_slot;
     mp.hhi = ws_at<uint16_t>(ws, pl.off_hhi); mp.hlo = ws_at<uint16_t>(ws, pl.off_hlo);
     mp.nact = ws_at<int32_t>(ws, pl.off_nact); mp.list = ws_at<uint8_t>(ws, pl.off_list);
-    mp.mask_bits = a->mask_bits; mp.union_words = union_words; mp.partial = partial;
+    mp.mask_bits = a->mask_bits; mp.union_words = union_words; mp.partial = partial; mp.npc = npc; mp.NCT = pl.NCT;
     mp.union_idx = a->union_idx; mp.union_cnt = a->union_cnt;
     mp.H = pl.H; mp.E = pl.E; mp.I = pl.I; mp.Is = pl.Is; mp.S = pl.S; mp.W = pl.W; mp.Imax = pl.Imax;
     mp.slots = pl.slots; mp.NT = pl.NT; mp.max_items = pl.max_items;
@@ -283,7 +281,8 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     DownParams dp{};
     dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
     dp.hdr = hdr; dp.counts = counts; dp.offsets = offsets; dp.touched = touched; dp.slot_n = slot_n; dp.slot_off = slot_off;
-    dp.union_words = union_words; dp.ucount = ucount; dp.partial = partial; dp.sched = sched;
+    dp.union_words = union_words; dp.ucount = ucount; dp.partial = partial; dp.npc = npc;
+    dp.pair_tok = pair_tok; dp.pair_slot = pair_slot; dp.slots = pl.slots;
     dp.union_idx = a->union_idx; dp.union_cnt = a->union_cnt;
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
     dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.KMAX = pl.KMAX;
@@ -291,10 +290,8 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     if (launch_down(pl, dp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
-    cp.partial = partial; cp.topk_w = w; cp.topk_ids = ids; cp.counts = counts; cp.offsets = offsets;
-    cp.pos = pos; cp.sched = sched; cp.y = a->y;
-    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.E = pl.E; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT;
-    cp.nm = pl.nm;
+    cp.partial = partial; cp.topk_w = w; cp.npc = npc; cp.y = a->y;
+    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -329,7 +326,6 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     int32_t *slot_off = ws_at<int32_t>(workspace, pl.off_slotoff);
     int32_t *pair_tok = ws_at<int32_t>(workspace, pl.off_pair_tok);
     int32_t *pair_slot = ws_at<int32_t>(workspace, pl.off_pair_slot);
-    int32_t *pos = ws_at<int32_t>(workspace, pl.off_pos);
     float *scores = ws_at<float>(workspace, pl.off_h);
     float *taus = ws_at<float>(workspace, pl.off_taus);
 
@@ -337,7 +333,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.ids = ids;
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
-    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.pos = pos; gp.union_cnt = nullptr;
+    gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr;
     if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 

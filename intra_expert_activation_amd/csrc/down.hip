@@ -255,7 +255,7 @@ struct DownLds {
 // piece k.
 template <class Tr, int TB, int MODE>
 __device__ __forceinline__ void down_piece(const DownParams &p, const uint16_t *list, int xe, int n, int off,
-                                           int tile, int ctg, int a, int b, int k, int lane, int wave)
+                                           int tile, int ctg, int a, int b, int k, bool last, int lane, int wave)
 {
     using V = typename Tr::V;
     constexpr int EPL = Tr::kEpl;                    // 4 columns per lane
@@ -269,7 +269,9 @@ __device__ __forceinline__ void down_piece(const DownParams &p, const uint16_t *
     const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
     const V *Wd = reinterpret_cast<const V *>(shared ? p.swd : p.wd) + mat + v0;
     const float *hb = p.h + (shared ? (size_t)p.A * p.I + (size_t)(off - p.A) * Ie : (size_t)off * Ie);
-
+    // lane t < nt: the output row (t * slots + slot) of the tile's pair t
+    const int pr = off + t0 + min(lane, nt - 1);
+    const int orow = p.pair_tok[pr] * p.slots + p.pair_slot[pr];
 
     float acc[TB][EPL];
 #pragma unroll
@@ -278,14 +280,18 @@ __device__ __forceinline__ void down_piece(const DownParams &p, const uint16_t *
         for (int c = 0; c < EPL; ++c) acc[t][c] = 0.f;
     down_stream<Tr, TB, MODE>(Wd, rowV, hb, n, t0, nt, list, a, b - a, acc, lane);
 
-    float *dst = p.partial + ((size_t)k * p.P + off + t0) * p.H + (size_t)(v0 + lane) * EPL;
+    float *dst = p.partial + (size_t)k * p.P * p.H + (size_t)(v0 + lane) * EPL;
 #pragma unroll
     for (int t = 0; t < TB; ++t)
-        if (t < nt)
+        if (t < nt) {
+            const int r = __builtin_amdgcn_readlane(orow, t);
 #pragma unroll
             for (int c = 0; c < EPL; c += 4)
-                *reinterpret_cast<float4 *>(dst + (size_t)t * p.H + c) =
+                *reinterpret_cast<float4 *>(dst + (size_t)r * p.H + c) =
                     make_float4(acc[t][c], acc[t][c + 1], acc[t][c + 2], acc[t][c + 3]);
+        }
+    // the group's last piece records how many pieces it has
+    if (last && wave == 0 && lane < nt) p.npc[(size_t)orow * p.NCT + ctg] = k + 1;
 }
 
 // Block-wide exclusive scan of v (one value per thread), with the total and
@@ -331,14 +337,23 @@ __device__ __forceinline__ void down_gemv(const DownParams &p, DownLds &D, int g
             const int n = p.slot_n[s];
             const int of = p.slot_off[s];
             const int uc = MODE == MOE_DENSE ? 0 : p.ucount[s];
+            const int Iw = xe >= p.E ? p.Is : p.I;
             D.xe[s] = xe;
             D.n[s] = n;
             D.off[s] = of;
             if (n < p.nm) {
-                const int U = (MODE == MOE_DENSE) ? (xe >= p.E ? p.Is : p.I) : uc;
+                const int U = (MODE == MOE_DENSE) ? Iw : uc;
                 ul[r] = U;
                 wl[r] = U * ((n + kDownTok - 1) / kDownTok);
-                if (g == 0 && p.union_cnt) p.union_cnt[xe] = U;
+                if (g == 0) {
+                    if (p.union_cnt) p.union_cnt[xe] = U;
+                    // no active row: no piece, the pairs' outputs are zero
+                    if (U == 0)
+                        for (int i = 0; i < n; ++i) {
+                            const int orow = p.pair_tok[of + i] * p.slots + p.pair_slot[of + i];
+                            for (int c = 0; c < p.NCT; ++c) p.npc[(size_t)orow * p.NCT + c] = 0;
+                        }
+                }
             }
         }
     }
@@ -358,18 +373,6 @@ __device__ __forceinline__ void down_gemv(const DownParams &p, DownLds &D, int g
     share = max(share, (long long)kMinShare);
     share = min(share, (long long)kDownChunk);
     share = max(share, (long long)((umax + p.KMAX - 2) / (p.KMAX - 1)));
-    if (g == 0) {
-        if (threadIdx.x == 0) p.sched[0] = (int)share;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int s = 2 * threadIdx.x + r;
-            if (s < ntouched) {
-                const int xe = p.touched[s];
-                p.sched[kSchedHdr + xe] = ex + (r ? wl[0] : 0);
-                p.sched[kSchedHdr + EX + xe] = ul[r];
-            }
-        }
-    }
     __syncthreads();
 
     // ---- workgroup shares vg = g + j GD: [vg share, (vg + 1) share) ---------
@@ -452,11 +455,12 @@ __device__ __forceinline__ void down_gemv(const DownParams &p, DownLds &D, int g
                 const int b = __builtin_amdgcn_readfirstlane(pc[j].b);
                 const int k = __builtin_amdgcn_readfirstlane(pc[j].k);
                 const int lo = __builtin_amdgcn_readfirstlane(pc[j].lofs);
+                const bool last = b == __builtin_amdgcn_readfirstlane(D.uc[s]);
                 const int nt = min(n - tile * kDownTok, kDownTok);
-                if (nt > 4) down_piece<DV, 8, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
-                else if (nt > 2) down_piece<DV, 4, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
-                else if (nt > 1) down_piece<DV, 2, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
-                else down_piece<DV, 1, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, lane, wave);
+                if (nt > 4) down_piece<DV, 8, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, last, lane, wave);
+                else if (nt > 2) down_piece<DV, 4, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, last, lane, wave);
+                else if (nt > 1) down_piece<DV, 2, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, last, lane, wave);
+                else down_piece<DV, 1, MODE>(p, list + lo, xe, n, of, tile, ctg, a, b, k, last, lane, wave);
             }
             // the union list output, after the round's streaming
             if (wave == 0 && p.union_idx)
@@ -556,67 +560,47 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 }
 
 // ---------------------------------------------------------------------------
-// k_combine: y[t] = sum_{k<K} w[t,k] * o[pos(t,k)] + sum_{s<S} o[pos(t,K+s)].
+// k_combine: y[t] = sum_{k<K} w[t,k] * o[t,k] + sum_{s<S} o[t,K+s].
 // o of a GEMV expert's pair is the sum, in piece order, of the partial sums of
-// the pieces its group (token tile, column tile) was cut into; an MFMA expert
-// writes piece 0 only.  A workgroup covers one token and one 256-column tile:
+// the pieces its group (token tile, column tile) was cut into (npc of them);
+// an MFMA expert writes piece 0 only.  A workgroup covers one token and one 256-column tile:
 // 64 column quads x 4 thread groups; group g adds the slots k with k % 4 == g,
 // and the 4 group sums meet in LDS in a fixed order (so the result is
 // deterministic).
 // ---------------------------------------------------------------------------
 // NB: slots per thread group whose loads are issued together (1, 2 or 4).
+// Each slot's weight, piece count and first piece depend on (t, slot) alone,
+// so a batch needs one memory latency (and one more for any further pieces).
 template <int NB>
 __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_acc)[3][64])
 {
-    constexpr int kCombBatch = NB;
     const int t = blockIdx.x;
     const int ct = blockIdx.y;
     const int q = threadIdx.x & 63;  // column quad within the tile
     const int g = threadIdx.x >> 6;  // slot group
     const int c4 = ct * 64 + q;
-    const int EX = p.E + (p.slots - p.K);
-    const long long share = p.sched[0];
     const int ctg = c4 / (kDownCols / 4);  // the down kernel's column tile of these columns
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-    // slots k = g, g + 4, ... in batches of kCombBatch: each batch's metadata,
-    // then its partial sums, are loaded as independent loads (a few memory
-    // latencies per batch instead of a chain per slot)
-    for (int k0 = g; k0 < p.slots; k0 += 4 * kCombBatch) {
-        int e[kCombBatch], pr[kCombBatch], np[kCombBatch];
-        float wk[kCombBatch];
+    for (int k0 = g; k0 < p.slots; k0 += 4 * NB) {
+        int np[NB];
+        float wk[NB];
+        float4 o[NB];
 #pragma unroll
-        for (int j = 0; j < kCombBatch; ++j) {
+        for (int j = 0; j < NB; ++j) {
             const int k = min(k0 + 4 * j, p.slots - 1);
-            const int rid = p.topk_ids[(size_t)t * p.K + min(k, p.K - 1)];
+            const int orow = t * p.slots + k;
             const float rw = p.topk_w[(size_t)t * p.K + min(k, p.K - 1)];
-            e[j] = (k < p.K) ? rid : p.E + (k - p.K);
             wk[j] = (k < p.K) ? rw : 1.f;
-            pr[j] = p.pos[(size_t)t * p.slots + k];
+            np[j] = p.npc[(size_t)orow * p.NCT + ctg];
+            o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)orow * p.H)[c4];
         }
 #pragma unroll
-        for (int j = 0; j < kCombBatch; ++j) {
-            const int cnt = p.counts[e[j]];
-            const int U = p.sched[kSchedHdr + EX + e[j]];
-            const int st = p.sched[kSchedHdr + e[j]];
-            const int of = p.offsets[e[j]];
-            int n = 1;  // an MFMA expert writes piece 0 only
-            if (cnt < p.nm) {
-                const int tile = (pr[j] - of) / kDownTok;
-                const long long gstart = (long long)p.NCT * st + (long long)(tile * p.NCT + ctg) * U;
-                n = U > 0 ? (int)((gstart + U - 1) / share - gstart / share) + 1 : 0;
-            }
-            np[j] = n;
-        }
-        float4 o[kCombBatch];
-#pragma unroll
-        for (int j = 0; j < kCombBatch; ++j)
-            o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)pr[j] * p.H)[c4];
-#pragma unroll
-        for (int j = 0; j < kCombBatch; ++j) {
+        for (int j = 0; j < NB; ++j) {
             if (k0 + 4 * j >= p.slots) break;
+            const int orow = t * p.slots + k0 + 4 * j;
             float4 v = np[j] > 0 ? o[j] : make_float4(0.f, 0.f, 0.f, 0.f);  // no piece: o = 0
             for (int kk = 1; kk < np[j]; ++kk) {
-                const float4 w = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + pr[j]) * p.H)[c4];
+                const float4 w = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + orow) * p.H)[c4];
                 v.x += w.x;
                 v.y += w.y;
                 v.z += w.z;

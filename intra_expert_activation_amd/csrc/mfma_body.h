@@ -178,6 +178,7 @@ struct MfmaDownLds {
     uint8_t sList[kDSeg][kTN];       // active rows of the segment's neuron tiles
     int sNact[kDSeg];
     int s_wpre[4];
+    int sRow[kTM];                   // output row (t * slots + slot) of each pair of the tile
 };
 
 typedef short bf16x4_bits_t __attribute__((ext_vector_type(4)));
@@ -339,9 +340,9 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     auto &sNact = S.sNact;
     auto &s_wpre = S.s_wpre;
 
-    const int NCT = p.H / kTC;
+    const int nct = p.H / kTC;
     const int L = xcd_remap(b, nblocks);
-    if (L >= p.max_items * NCT) return;
+    if (L >= p.max_items * nct) return;
     const int ct = L / p.max_items, item = L - ct * p.max_items;
     if (item >= p.hdr[1]) return;
     const int code = p.items[item];
@@ -361,6 +362,10 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     const int hr = tid >> 3, hc = (tid & 7) * 8;
     const int wr = tid >> 4, wc = (tid & 15) * 8;
 
+    if (tid < kTM) {
+        const int pr = off + m0 + min(tid, mt - 1);
+        S.sRow[tid] = p.pair_tok[pr] * p.slots + p.pair_slot[pr];
+    }
     f32x16_t acc[2] = {};
     for (int seg = 0; seg < NTe; seg += kDSeg) {
         const int ns = min(kDSeg, NTe - seg);
@@ -431,8 +436,10 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
         for (int r = 0; r < 16; ++r) {
             const int m = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int col = c0 + 64 * wn + 32 * nb + (lane & 31);
-            if (m < mt) p.partial[(size_t)(off + m0 + m) * H + col] = acc[nb][r];
+            if (m < mt) p.partial[(size_t)S.sRow[m] * H + col] = acc[nb][r];
         }
+    // one piece per pair and 1024-column tile (recorded by its first 128-column tile)
+    if (c0 % 1024 == 0 && tid < mt) p.npc[(size_t)S.sRow[tid] * p.NCT + c0 / 1024] = 1;
 
     // the expert's union list (complete: every projection tile has finished)
     if (tile == 0 && ct == 0 && (p.union_idx || p.union_cnt)) {

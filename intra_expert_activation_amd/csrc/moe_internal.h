@@ -49,7 +49,7 @@ struct Plan {
     int max_items;   // upper bound on (expert, 64-token tile) work items
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
-    size_t off_pair_tok, off_pair_slot, off_pos, off_union, off_ucount, off_sched, off_h, off_partial;
+    size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
     size_t off_taus;
     size_t off_items, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
@@ -73,7 +73,6 @@ struct GroupParams {
     int32_t *slot_off;    // [EX], first grouped pair of touched[s]
     int32_t *pair_tok;    // [P] token of the pair at each grouped position
     int32_t *pair_slot;   // [P] slot of the pair
-    int32_t *pos;         // [T*slots] grouped position of (t, slot)
     int32_t *union_cnt;   // optional output, zeroed for untouched experts
     uint32_t *union_words;// [EX,W], zeroed for the experts on the MFMA path
     int32_t *ucount;      // [EX] union sizes of the GEMV experts by touched slot, zeroed here
@@ -95,10 +94,6 @@ struct ProjParams {
     int nm;               // experts with nm or more pairs take the MFMA path
 };
 
-// Down projection schedule, written by GEMV down workgroup 0 and read by the
-// combine: [0] = share (work units per workgroup), [4 + xe] = first work unit
-// of expert xe (in units of its union rows), [4 + EX + xe] = its union size.
-constexpr int kSchedHdr = 4;
 constexpr int kDownChunk = 1024;  // largest share of a down wavefront (union rows)
 
 struct DownParams {
@@ -107,23 +102,24 @@ struct DownParams {
     const int32_t *hdr, *counts, *offsets, *touched, *slot_n, *slot_off;
     const uint32_t *union_words;
     const int32_t *ucount;  // by touched slot
+    const int32_t *pair_tok, *pair_slot;
+    // down output of pair (t, slot): piece k of its 1024-column tile c is
+    // partial[k][t * slots + slot][c * 1024 ...], npc[(t * slots + slot) * NCT + c]
+    // pieces (0: no active row, the output is zero)
     float *partial;       // [KMAX, P, H]
-    int32_t *sched;       // [kSchedHdr + 2 EX]
+    int32_t *npc;         // [P, NCT]
     int32_t *union_idx;   // optional output [EX, Imax]
     int32_t *union_cnt;   // optional output [EX]
-    int H, E, I, Is, S, A, P, W, Imax, NCT, KMAX, GD;
+    int H, E, I, Is, S, A, P, W, Imax, NCT, KMAX, GD, slots;
     int nm;
 };
 
 struct CombineParams {
-    const float *partial;
+    const float *partial; // as DownParams
     const float *topk_w;
-    const int32_t *topk_ids, *counts, *offsets;
-    const int32_t *pos;
-    const int32_t *sched;
+    const int32_t *npc;   // as DownParams
     float *y;
-    int T, H, K, E, slots, P, NCT;
-    int nm;               // MFMA experts write piece 0 only
+    int T, H, K, slots, P, NCT;
 };
 
 struct MfmaParams {
@@ -134,9 +130,10 @@ struct MfmaParams {
     int32_t *nact;        // active rows per (item, neuron tile)
     uint8_t *list;        // their offsets within the tile, ascending
     uint32_t *mask_bits, *union_words;
-    float *partial;
+    float *partial;       // as DownParams (piece 0 only)
+    int32_t *npc;         // as DownParams
     int32_t *union_idx, *union_cnt;
-    int H, E, I, Is, S, W, Imax, slots, NT, max_items;
+    int H, E, I, Is, S, W, Imax, slots, NT, max_items, NCT;
 };
 
 struct SelectParams {

@@ -295,7 +295,6 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
                 const int t = a / p.K, k = a - t * p.K;
                 p.pair_tok[pos] = t;
                 p.pair_slot[pos] = k;
-                p.pos[(size_t)t * p.slots + k] = pos;
             }
         }
     }
@@ -305,7 +304,6 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         const int pos = p.A + i;
         p.pair_tok[pos] = t;
         p.pair_slot[pos] = p.K + s;
-        p.pos[(size_t)t * p.slots + p.K + s] = pos;
     }
 }
 
