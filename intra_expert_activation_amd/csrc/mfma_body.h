@@ -157,10 +157,100 @@ __device__ __forceinline__ void gemm_64x64(f32x16_t &acc, uint16_t (*sX)[kRow], 
 #undef MOE_GEMM_LOAD
 #undef MOE_GEMM_STORE
 
+// Gate and up products of the same 64 x 64 tile in one pass over K:
+// G += X[rows sTok] * Wg[r]^T and U += X[rows sTok] * Wu[r]^T for the tile's
+// rows r < nrows (rows past nrows load row 0 and feed unused entries).  Each
+// chunk of X is loaded once for both.  Same pipeline as gemm_64x64: two chunks
+// in flight in registers while the MFMAs read the one in LDS.
+#define MOE_GEMM2_LOAD(X0, X1, G0, G1, U0, U1, c)                         \
+    do {                                                                  \
+        X0 = *reinterpret_cast<const uint4 *>(xp0 + (c) * kKC);           \
+        X1 = *reinterpret_cast<const uint4 *>(xp1 + (c) * kKC);           \
+        G0 = *reinterpret_cast<const uint4 *>(gp0 + (c) * kKC);           \
+        G1 = *reinterpret_cast<const uint4 *>(gp1 + (c) * kKC);           \
+        U0 = *reinterpret_cast<const uint4 *>(up0 + (c) * kKC);           \
+        U1 = *reinterpret_cast<const uint4 *>(up1 + (c) * kKC);           \
+    } while (0)
+#define MOE_GEMM2_STORE(X0, X1, G0, G1, U0, U1)                           \
+    do {                                                                  \
+        *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = X0;                  \
+        *reinterpret_cast<uint4 *>(&sX[r + 32][c8 * 8]) = X1;             \
+        *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = G0;                  \
+        *reinterpret_cast<uint4 *>(&sW[r + 32][c8 * 8]) = G1;             \
+        *reinterpret_cast<uint4 *>(&sU[r][c8 * 8]) = U0;                  \
+        *reinterpret_cast<uint4 *>(&sU[r + 32][c8 * 8]) = U1;             \
+    } while (0)
+
+__device__ __forceinline__ void gemm2_mma(f32x16_t &accg, f32x16_t &accu, uint16_t (*sX)[kRow],
+                                          uint16_t (*sW)[kRow], uint16_t (*sU)[kRow], int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int s = 0; s < kKC / 16; ++s) {
+        const int k = 16 * s + 8 * (lane >> 5);
+        const bf16x8_t a = lds_frag(sX[32 * wm + (lane & 31)], k);
+        const bf16x8_t g = lds_frag(sW[32 * wn + (lane & 31)], k);
+        const bf16x8_t u = lds_frag(sU[32 * wn + (lane & 31)], k);
+        accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, g, accg, 0, 0, 0);
+        accu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, u, accu, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void gemm2_64x64(f32x16_t &accg, f32x16_t &accu, uint16_t (*sX)[kRow],
+                                            uint16_t (*sW)[kRow], uint16_t (*sU)[kRow], const uint16_t *X,
+                                            const int *sTok, const uint16_t *Wg, const uint16_t *Wu, int nrows,
+                                            int H)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int r = tid >> 3, c8 = tid & 7;
+    const int t0 = sTok[r], t1 = sTok[r + 32];
+    const int w0 = r < nrows ? r : 0, w1 = r + 32 < nrows ? r + 32 : 0;
+    const uint16_t *xp0 = X + (size_t)(t0 >= 0 ? t0 : 0) * H + c8 * 8;
+    const uint16_t *xp1 = X + (size_t)(t1 >= 0 ? t1 : 0) * H + c8 * 8;
+    const uint16_t *gp0 = Wg + (size_t)w0 * H + c8 * 8;
+    const uint16_t *gp1 = Wg + (size_t)w1 * H + c8 * 8;
+    const uint16_t *up0 = Wu + (size_t)w0 * H + c8 * 8;
+    const uint16_t *up1 = Wu + (size_t)w1 * H + c8 * 8;
+    const int NC = H / kKC;
+    uint4 ax0, ax1, ag0, ag1, au0, au1, bx0, bx1, bg0, bg1, bu0, bu1;
+    MOE_GEMM2_LOAD(ax0, ax1, ag0, ag1, au0, au1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_GEMM2_LOAD(bx0, bx1, bg0, bg1, bu0, bu1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    int c = 0;
+#pragma unroll 1
+    for (; c + 2 < NC; c += 2) {
+        MOE_GEMM2_STORE(ax0, ax1, ag0, ag1, au0, au1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_GEMM2_LOAD(ax0, ax1, ag0, ag1, au0, au1, c + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
+        __syncthreads();
+        MOE_GEMM2_STORE(bx0, bx1, bg0, bg1, bu0, bu1);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_GEMM2_LOAD(bx0, bx1, bg0, bg1, bu0, bu1, c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
+        __syncthreads();
+    }
+    MOE_GEMM2_STORE(ax0, ax1, ag0, ag1, au0, au1);
+    __syncthreads();
+    gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
+    __syncthreads();
+    MOE_GEMM2_STORE(bx0, bx1, bg0, bg1, bu0, bu1);
+    __syncthreads();
+    gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
+    __syncthreads();
+}
+#undef MOE_GEMM2_LOAD
+#undef MOE_GEMM2_STORE
+
 struct MfmaProjLds {
     uint16_t sX[kTM][kRow];
     uint16_t sW[kTN][kRow];
-    float sA[kTM][kTN + 1];
+    uint16_t sU[kTN][kRow];
     uint32_t sMask[kTM][2];
     uint32_t sAct[2];
     int sTok[kTM];
@@ -203,12 +293,21 @@ __device__ __forceinline__ bf16x8_t lds_frag_tr(const uint16_t *tile, int ld, in
 
 // Projection of one (item, 64-neuron tile); `b` and `nblocks` are this
 // workgroup's index among the MFMA workgroups and their count (a multiple of 8).
+// The gate and up products are computed together in one pass over the token
+// tile's hidden states (up for every row of the tile: at 32 or more tokens the
+// tile's union covers most rows, and a second pass over X for the active rows
+// alone read more bytes than it skipped); h keeps the sparse definition, with
+// an inactive (token, neuron) set to exactly 0 by a select, and only the
+// tile's active rows are stored, compacted, for the down projection.  Work
+// items run item-major (the neuron tiles of one token tile next to each other
+// on one XCD, sharing its hidden states in L2, then the expert's next token
+// tile, sharing the weight tiles).
 template <int MODE>
 __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds &S, int b, int nblocks)
 {
     auto &sX = S.sX;
     auto &sW = S.sW;
-    auto &sA = S.sA;
+    auto &sU = S.sU;
     auto &sMask = S.sMask;
     auto &sAct = S.sAct;
     auto &sTok = S.sTok;
@@ -217,7 +316,7 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
 
     const int L = xcd_remap(b, nblocks);
     if (L >= p.max_items * p.NT) return;
-    const int nt = L / p.max_items, item = L - nt * p.max_items;
+    const int item = L / p.NT, nt = L - item * p.NT;
     if (item >= p.hdr[1]) return;
     const int code = p.items[item];
     const int xe = code >> 16, tile = code & 0xffff;
@@ -241,26 +340,29 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
     if (tid < 2 * kTM) sMask[tid >> 1][tid & 1] = 0u;
     __syncthreads();
 
-    // ---- gate ---------------------------------------------------------------
-    f32x16_t acc = {};
-    gemm_64x64(acc, sX, sW, p.x, sTok, Wg, [&](int r) { return r < nrows ? r : -1; }, H, true);
+    // ---- gate and up ----------------------------------------------------------
+    f32x16_t accg = {}, accu = {};
+    gemm2_64x64(accg, accu, sX, sW, sU, p.x, sTok, Wg, Wu, nrows, H);
 
-    uint32_t actw = 0;
+    // lane (r, lane) holds token m = 32 wm + 8 (r / 4) + 4 (lane / 32) + r % 4 and
+    // row nn = 32 wn + lane % 32 of both products
+    const int nn = 32 * wn + (lane & 31);
+    uint32_t actw = 0, mine = 0;  // mine: bit r = this lane's (m, nn) is active
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int mlo = 32 * wm + 8 * (r >> 2) + (r & 3);  // token of lanes 0..31; lanes 32..63 hold mlo + 4
         const int m = mlo + 4 * (lane >> 5);
-        const int nn = 32 * wn + (lane & 31);
-        const float a = silu(acc[r]);
+        const float a = silu(accg[r]);
         const bool valid = m < mt && nn < nrows;
         const bool act = valid && (MODE == MOE_DENSE || !(fabsf(a) < tau));
-        sA[m][nn] = a;
-        const uint64_t b = __ballot(act);
+        accg[r] = a;
+        mine |= (uint32_t)act << r;
+        const uint64_t bb = __ballot(act);
         if (lane == 0) {
-            sMask[mlo][wn] = (uint32_t)b;
-            sMask[mlo + 4][wn] = (uint32_t)(b >> 32);
+            sMask[mlo][wn] = (uint32_t)bb;
+            sMask[mlo + 4][wn] = (uint32_t)(bb >> 32);
         }
-        actw |= (uint32_t)b | (uint32_t)(b >> 32);
+        actw |= (uint32_t)bb | (uint32_t)(bb >> 32);
     }
     if (lane == 0 && actw) atomicOr(&sAct[wn], actw);
     __syncthreads();
@@ -284,40 +386,37 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
         if (sAct[0]) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5)], sAct[0]);
         if (nrows > 32 && sAct[1]) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5) + 1], sAct[1]);
     }
+    const uint64_t act64 = (uint64_t)sAct[0] | ((uint64_t)sAct[1] << 32);
+    const int nact = __popcll(act64);
     if (wave == 0) {
-        const uint64_t act64 = (uint64_t)sAct[0] | ((uint64_t)sAct[1] << 32);
         const bool bit = (act64 >> lane) & 1ull;
-        const uint64_t b = __ballot(bit);
-        if (bit) sList[__popcll(b & lanemask_lt())] = lane;
-        if (lane == 0) sNact = __popcll(b);
+        if (bit) sList[__popcll(act64 & lanemask_lt())] = lane;
     }
     __syncthreads();
-    const int nact = sNact;
     if (tid == 0) p.nact[blk] = nact;
     if (tid < nact) p.list[(size_t)blk * kTN + tid] = (uint8_t)sList[tid];
     if (nact == 0) return;
 
-    // ---- up, over the active rows only ---------------------------------------
-    const int nup = nact <= 32 ? 32 : 64;
-    f32x16_t accu = {};
-    gemm_64x64(accu, sX, sW, p.x, sTok, Wu, [&](int r) { return r < nact ? sList[r] : -1; }, H,
-               32 * wn < nup);
-    if (32 * wn < nup) {
-        uint16_t *hhi = p.hhi + (size_t)blk * kTM * kTN;
-        uint16_t *hlo = p.hlo + (size_t)blk * kTM * kTN;
+    // ---- h of the active rows, compacted -------------------------------------
+    // active row nn goes to column (its rank among the active rows, < nact);
+    // the lane of row nn >= nact also zeroes column nn, so every column of the
+    // block is written (the down product reads zeros past nact)
+    const bool row_act = (act64 >> nn) & 1ull;
+    const int col = __popcll(act64 & ((1ull << nn) - 1ull));
+    uint16_t *hhi = p.hhi + (size_t)blk * kTM * kTN;
+    uint16_t *hlo = p.hlo + (size_t)blk * kTM * kTN;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int c = 32 * wn + (lane & 31);
-            float hv = 0.f;
-            if (c < nact && m < mt) {
-                const int j = sList[c];
-                const bool mb = (sMask[m][j >> 5] >> (j & 31)) & 1u;
-                hv = mb ? sA[m][j] * accu[r] : 0.f;  // a select: inactive neurons add exactly 0
-            }
+    for (int r = 0; r < 16; ++r) {
+        const int m = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row_act) {
+            const float hv = ((mine >> r) & 1u) ? accg[r] * accu[r] : 0.f;  // a select: inactive adds exactly 0
             const uint16_t hi = bf16_rne(hv);
-            hhi[m * kTN + c] = hi;
-            hlo[m * kTN + c] = bf16_rne(hv - bf16_to_f32(hi));
+            hhi[m * kTN + col] = hi;
+            hlo[m * kTN + col] = bf16_rne(hv - bf16_to_f32(hi));
+        }
+        if (nn >= nact) {
+            hhi[m * kTN + nn] = 0;
+            hlo[m * kTN + nn] = 0;
         }
     }
 }
