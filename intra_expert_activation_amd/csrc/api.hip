@@ -95,12 +95,15 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->use_mfma = 0;
     p->NT = (p->Imax + 63) / 64;
     p->max_items = 0;
+    p->max_pairs = 0;
     if (!calib && p->dtype == MOE_BF16 && T >= kMfmaMinPairs) {
         p->nm = kMfmaMinPairs;
         p->use_mfma = 1;
         // sum over experts of ceil(n_e / 64) <= A/64 + (number of such experts)
         const int big = (p->A / p->nm < p->E ? p->A / p->nm : p->E);
         p->max_items = p->A / kMfmaTokens + big + p->S * ((T + kMfmaTokens - 1) / kMfmaTokens);
+        // an expert with k tiles has ceil(k / 2) pairs
+        p->max_pairs = (p->max_items + big + p->S + 1) / 2;
     }
 
     // workspace layout
@@ -128,6 +131,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_taus = take((size_t)(2 + p->EX) * 4);
     const size_t blocks = (size_t)p->max_items * p->NT;
     p->off_items = take((size_t)p->max_items * 4);
+    p->off_pairs = take((size_t)p->max_pairs * 4);
     p->off_nact = take(blocks * 4);
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);
@@ -245,6 +249,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.W = pl.W;
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
+    gp.pairs = ws_at<int32_t>(ws, pl.off_pairs);
     if (launch_route_group(a->router_logits, pl.renorm, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
@@ -263,6 +268,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     mp.swg = (const uint16_t *)a->ws_gate; mp.swu = (const uint16_t *)a->ws_up; mp.swd = (const uint16_t *)a->ws_down;
     mp.tau = a->tau;
     mp.hdr = hdr; mp.counts = counts; mp.offsets = offsets; mp.items = ws_at<int32_t>(ws, pl.off_items);
+    mp.pairs = ws_at<int32_t>(ws, pl.off_pairs); mp.max_pairs = pl.max_pairs;
     mp.pair_tok = pair_tok; mp.pair_slot = pair_slot;
     mp.hhi = ws_at<uint16_t>(ws, pl.off_hhi); mp.hlo = ws_at<uint16_t>(ws, pl.off_hlo);
     mp.nact = ws_at<int32_t>(ws, pl.off_nact); mp.list = ws_at<uint8_t>(ws, pl.off_list);
@@ -334,7 +340,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.T = pl.T; gp.K = pl.K; gp.E = pl.E; gp.S = pl.S; gp.A = pl.A; gp.P = pl.P; gp.slots = pl.slots;
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.union_cnt = nullptr;
-    gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr;
+    gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr; gp.pairs = nullptr;
     if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};

@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256, 3) void k_down_bf16(DownParams p, MfmaParams m
         MfmaDownLds mfma;
     } S;
     if ((int)blockIdx.x < p.GD) down_gemv<BF16, MODE>(p, S.gemv, blockIdx.x);
-    else mfma_down_body<MODE>(mp, S.mfma, blockIdx.x - p.GD, gridDim.x - p.GD);
+    else mfma_down_body<MODE>(mp, S.mfma, blockIdx.x - p.GD);
 }
 
 static int round8_down(long long v) { return (int)((v + 7) / 8 * 8); }

@@ -9,24 +9,25 @@
 // the kernel: the result is the same sparse function (the GEMV kernels and
 // these agree to rounding).
 //
-// Tiles.  A work item is (expert, tile of 64 of its tokens).
-//  k_proj_mfma  (item, 64-neuron tile): G = X W_gate^T over K = H with
-//               v_mfma_f32_32x32x16_bf16 (4 wavefronts in 2x2, 32x32 each),
-//               operands staged through LDS in 64-wide K chunks with the next
-//               chunk's global loads in flight; epilogue a = SiLU(g),
-//               m = NOT(|a| < tau), mask words by ballot, the tile's active
-//               rows (OR over its tokens) compacted in ascending order; then
-//               U = X W_up[active]^T over the active rows only, and
-//               h = m ? a*u : 0 stored compacted [64 tokens][active rows] as a
-//               bf16 pair (hi + lo, hi + lo = h to ~2^-17) so the down product
-//               keeps fp32-level accuracy.
+// Tiles.  A work item is (expert, tile of 64 of its tokens); the projection
+// takes them in pairs (two adjacent tiles of one expert, or its last alone).
+//  k_proj_mfma  (item pair, 64-neuron tile): G = X W_gate^T and U = X W_up^T
+//               over K = H together with v_mfma_f32_32x32x16_bf16 (4
+//               wavefronts in 2x2, each 64 tokens x 32 rows of both), operands
+//               staged through LDS in 64-wide K chunks with the next chunk's
+//               global loads in flight; epilogue a = SiLU(g),
+//               m = NOT(|a| < tau), mask words by ballot, each 64-token tile's
+//               active rows (OR over its tokens) compacted in ascending order,
+//               and h = m ? a*u : 0 of those rows stored compacted
+//               [64 tokens][active rows] as a bf16 pair (hi + lo = h to
+//               ~2^-17) so the down product keeps fp32-level accuracy.
 //  k_down_mfma  (item, 128-column tile): O = sum over neuron tiles of
 //               H_tile[64 x active] * W_down[active rows, 128 cols]; the
-//               neuron-major down rows are transposed into LDS (k-contiguous)
-//               for the MFMA B operand.  One output per pair (no split).
+//               neuron-major down rows are staged row-major in LDS and read
+//               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
+//               output per pair (no split).
 // Work indices are remapped so that each XCD (8 per MI355X, each with its own
-// L2) runs a contiguous range: the token tiles of one expert, which read the
-// same weight rows, then share that L2.
+// L2) runs a contiguous range of the work units that exist.
 #include "mfma_body.h"
 
 namespace moe {
@@ -35,17 +36,17 @@ namespace moe {
 // 256 threads wide (H below 2048 in bf16): the merged kernels host these
 // bodies otherwise.
 template <int MODE>
-__global__ __launch_bounds__(256) void k_proj_mfma(MfmaParams p)
+__global__ __launch_bounds__(256, 3) void k_proj_mfma(MfmaParams p)
 {
     __shared__ MfmaProjLds S;
-    mfma_proj_body<MODE>(p, S, blockIdx.x, gridDim.x);
+    mfma_proj_body<MODE>(p, S, blockIdx.x);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256) void k_down_mfma(MfmaParams p)
 {
     __shared__ MfmaDownLds S;
-    mfma_down_body<MODE>(p, S, blockIdx.x, gridDim.x);
+    mfma_down_body<MODE>(p, S, blockIdx.x);
 }
 
 static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
@@ -53,7 +54,7 @@ static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
 hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t st)
 {
     if (!pl.use_mfma) return hipSuccess;
-    const dim3 grid(round8((long long)pl.max_items * pl.NT)), block(256);
+    const dim3 grid(round8((long long)pl.max_pairs * pl.NT)), block(256);
     if (mode == MOE_DENSE) hipLaunchKernelGGL(k_proj_mfma<MOE_DENSE>, grid, block, 0, st, mp);
     else hipLaunchKernelGGL(k_proj_mfma<MOE_SPARSE>, grid, block, 0, st, mp);
     return hipGetLastError();

@@ -9,25 +9,25 @@
 // the kernel: the result is the same sparse function (the GEMV kernels and
 // these agree to rounding).
 //
-// Tiles.  A work item is (expert, tile of 64 of its tokens).
-//  k_proj_mfma  (item, 64-neuron tile): G = X W_gate^T over K = H with
-//               v_mfma_f32_32x32x16_bf16 (4 wavefronts in 2x2, 32x32 each),
-//               operands staged through LDS in 64-wide K chunks with the next
-//               chunk's global loads in flight; epilogue a = SiLU(g),
-//               m = NOT(|a| < tau), mask words by ballot, the tile's active
-//               rows (OR over its tokens) compacted in ascending order; then
-//               U = X W_up[active]^T over the active rows only, and
-//               h = m ? a*u : 0 stored compacted [64 tokens][active rows] as a
-//               bf16 pair (hi + lo, hi + lo = h to ~2^-17) so the down product
-//               keeps fp32-level accuracy.
+// Tiles.  A work item is (expert, tile of 64 of its tokens); the projection
+// takes them in pairs (two adjacent tiles of one expert, or its last alone).
+//  k_proj_mfma  (item pair, 64-neuron tile): G = X W_gate^T and U = X W_up^T
+//               over K = H together with v_mfma_f32_32x32x16_bf16 (4
+//               wavefronts in 2x2, each 64 tokens x 32 rows of both), operands
+//               staged through LDS in 64-wide K chunks with the next chunk's
+//               global loads in flight; epilogue a = SiLU(g),
+//               m = NOT(|a| < tau), mask words by ballot, each 64-token tile's
+//               active rows (OR over its tokens) compacted in ascending order,
+//               and h = m ? a*u : 0 of those rows stored compacted
+//               [64 tokens][active rows] as a bf16 pair (hi + lo = h to
+//               ~2^-17) so the down product keeps fp32-level accuracy.
 //  k_down_mfma  (item, 128-column tile): O = sum over neuron tiles of
 //               H_tile[64 x active] * W_down[active rows, 128 cols]; the
 //               neuron-major down rows are staged row-major in LDS and read
 //               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
 //               output per pair (no split).
 // Work indices are remapped so that each XCD (8 per MI355X, each with its own
-// L2) runs a contiguous range: the token tiles of one expert, which read the
-// same weight rows, then share that L2.
+// L2) runs a contiguous range of the work units that exist.
 #pragma once
 
 #include "moe_internal.h"
@@ -43,12 +43,18 @@ constexpr int kKC = 64;                 // K chunk staged in LDS
 constexpr int kRow = kKC + 8;           // padded LDS row (bf16 elements), 144 bytes
 constexpr int kTC = 128;                // output columns per down tile
 
-__device__ __forceinline__ int xcd_remap(int b, int nblocks)
+// Logical work index of workgroup b when nvalid work units exist (known on
+// the device only), or -1.  Consecutive workgroups are dispatched round-robin
+// over the 8 XCDs; XCD x takes the contiguous range [x * per, (x + 1) * per)
+// of the valid units, so neighbouring units share its L2 and every XCD gets
+// an equal share however many of the grid's workgroups have work.
+__device__ __forceinline__ int xcd_remap(int b, int nvalid)
 {
-    // consecutive workgroups are dispatched round-robin over the 8 XCDs; give
-    // XCD x the logical range [x*per, (x+1)*per) (nblocks is a multiple of 8)
-    const int per = nblocks / 8;
-    return (b % 8) * per + b / 8;
+    const int per = (nvalid + 7) / 8;
+    const int j = b >> 3;
+    if (j >= per) return -1;
+    const int L = (b & 7) * per + j;
+    return L < nvalid ? L : -1;
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f)
@@ -157,105 +163,97 @@ __device__ __forceinline__ void gemm_64x64(f32x16_t &acc, uint16_t (*sX)[kRow], 
 #undef MOE_GEMM_LOAD
 #undef MOE_GEMM_STORE
 
-// Gate and up products of the same 64 x 64 tile in one pass over K:
-// G += X[rows sTok] * Wg[r]^T and U += X[rows sTok] * Wu[r]^T for the tile's
-// rows r < nrows (rows past nrows load row 0 and feed unused entries).  Each
-// chunk of X is loaded once for both.  Same pipeline as gemm_64x64: two chunks
-// in flight in registers while the MFMAs read the one in LDS.
-#define MOE_GEMM2_LOAD(X0, X1, G0, G1, U0, U1, c)                         \
-    do {                                                                  \
-        X0 = *reinterpret_cast<const uint4 *>(xp0 + (c) * kKC);           \
-        X1 = *reinterpret_cast<const uint4 *>(xp1 + (c) * kKC);           \
-        G0 = *reinterpret_cast<const uint4 *>(gp0 + (c) * kKC);           \
-        G1 = *reinterpret_cast<const uint4 *>(gp1 + (c) * kKC);           \
-        U0 = *reinterpret_cast<const uint4 *>(up0 + (c) * kKC);           \
-        U1 = *reinterpret_cast<const uint4 *>(up1 + (c) * kKC);           \
-    } while (0)
-#define MOE_GEMM2_STORE(X0, X1, G0, G1, U0, U1)                           \
-    do {                                                                  \
-        *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = X0;                  \
-        *reinterpret_cast<uint4 *>(&sX[r + 32][c8 * 8]) = X1;             \
-        *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = G0;                  \
-        *reinterpret_cast<uint4 *>(&sW[r + 32][c8 * 8]) = G1;             \
-        *reinterpret_cast<uint4 *>(&sU[r][c8 * 8]) = U0;                  \
-        *reinterpret_cast<uint4 *>(&sU[r + 32][c8 * 8]) = U1;             \
-    } while (0)
-
-__device__ __forceinline__ void gemm2_mma(f32x16_t &accg, f32x16_t &accu, uint16_t (*sX)[kRow],
-                                          uint16_t (*sW)[kRow], uint16_t (*sU)[kRow], int wm, int wn, int lane)
+__device__ __forceinline__ void gemm2_mma(f32x16_t (&acc)[2][2], uint16_t (*sX)[kRow], uint16_t (*sW)[kRow],
+                                          uint16_t (*sU)[kRow], int wm, int wn, int lane)
 {
 #pragma unroll
     for (int s = 0; s < kKC / 16; ++s) {
         const int k = 16 * s + 8 * (lane >> 5);
-        const bf16x8_t a = lds_frag(sX[32 * wm + (lane & 31)], k);
+        const bf16x8_t a0 = lds_frag(sX[64 * wm + (lane & 31)], k);
+        const bf16x8_t a1 = lds_frag(sX[64 * wm + 32 + (lane & 31)], k);
         const bf16x8_t g = lds_frag(sW[32 * wn + (lane & 31)], k);
         const bf16x8_t u = lds_frag(sU[32 * wn + (lane & 31)], k);
-        accg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, g, accg, 0, 0, 0);
-        accu = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, u, accu, 0, 0, 0);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, g, acc[0][0], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, g, acc[1][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, u, acc[0][1], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, u, acc[1][1], 0, 0, 0);
     }
 }
 
-__device__ __forceinline__ void gemm2_64x64(f32x16_t &accg, f32x16_t &accu, uint16_t (*sX)[kRow],
-                                            uint16_t (*sW)[kRow], uint16_t (*sU)[kRow], const uint16_t *X,
-                                            const int *sTok, const uint16_t *Wg, const uint16_t *Wu, int nrows,
-                                            int H)
+// Gate and up products of a 128-token x 64-row tile in one pass over K:
+// acc[q][0] += X * Wg^T and acc[q][1] += X * Wu^T for this wavefront's 32
+// tokens 64 wm + 32 q + ... and 32 rows 32 wn + ...  Rows past nrows load row 0
+// and feed unused entries; token entries below 0 load token 0.  Each chunk of
+// X is loaded once for both products; the next chunk is in flight in
+// registers while the MFMAs read the current one in LDS (two chunks in flight
+// need 32 more registers, and measured slower at 2 workgroups per CU than one
+// at 3).
+__device__ __forceinline__ void gemm2_128x64(f32x16_t (&acc)[2][2], uint16_t (*sX)[kRow], uint16_t (*sW)[kRow],
+                                             uint16_t (*sU)[kRow], const uint16_t *X, const int *sTok,
+                                             const uint16_t *Wg, const uint16_t *Wu, int nrows, int H)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int r = tid >> 3, c8 = tid & 7;
-    const int t0 = sTok[r], t1 = sTok[r + 32];
-    const int w0 = r < nrows ? r : 0, w1 = r + 32 < nrows ? r + 32 : 0;
+    const int r = tid >> 3, c8 = tid & 7;  // rows r, r + 32, ... ; 16 bytes at column 8 c8
+    const int t0 = sTok[r], t1 = sTok[r + 32], t2 = sTok[r + 64], t3 = sTok[r + 96];
     const uint16_t *xp0 = X + (size_t)(t0 >= 0 ? t0 : 0) * H + c8 * 8;
     const uint16_t *xp1 = X + (size_t)(t1 >= 0 ? t1 : 0) * H + c8 * 8;
+    const uint16_t *xp2 = X + (size_t)(t2 >= 0 ? t2 : 0) * H + c8 * 8;
+    const uint16_t *xp3 = X + (size_t)(t3 >= 0 ? t3 : 0) * H + c8 * 8;
+    const int w0 = r < nrows ? r : 0, w1 = r + 32 < nrows ? r + 32 : 0;
     const uint16_t *gp0 = Wg + (size_t)w0 * H + c8 * 8;
     const uint16_t *gp1 = Wg + (size_t)w1 * H + c8 * 8;
     const uint16_t *up0 = Wu + (size_t)w0 * H + c8 * 8;
     const uint16_t *up1 = Wu + (size_t)w1 * H + c8 * 8;
     const int NC = H / kKC;
-    uint4 ax0, ax1, ag0, ag1, au0, au1, bx0, bx1, bg0, bg1, bu0, bu1;
-    MOE_GEMM2_LOAD(ax0, ax1, ag0, ag1, au0, au1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    MOE_GEMM2_LOAD(bx0, bx1, bg0, bg1, bu0, bu1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    int c = 0;
+    // a chunk, per thread: X rows r + 32 i (i < 4), Wg and Wu rows r, r + 32
+#define MOE_GEMM2_LOAD(V, c)                                                   \
+    do {                                                                       \
+        V##0 = *reinterpret_cast<const uint4 *>(xp0 + (c) * kKC);              \
+        V##1 = *reinterpret_cast<const uint4 *>(xp1 + (c) * kKC);              \
+        V##2 = *reinterpret_cast<const uint4 *>(xp2 + (c) * kKC);              \
+        V##3 = *reinterpret_cast<const uint4 *>(xp3 + (c) * kKC);              \
+        V##4 = *reinterpret_cast<const uint4 *>(gp0 + (c) * kKC);              \
+        V##5 = *reinterpret_cast<const uint4 *>(gp1 + (c) * kKC);              \
+        V##6 = *reinterpret_cast<const uint4 *>(up0 + (c) * kKC);              \
+        V##7 = *reinterpret_cast<const uint4 *>(up1 + (c) * kKC);              \
+    } while (0)
+#define MOE_GEMM2_STORE(V)                                                     \
+    do {                                                                       \
+        *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = V##0;                     \
+        *reinterpret_cast<uint4 *>(&sX[r + 32][c8 * 8]) = V##1;                \
+        *reinterpret_cast<uint4 *>(&sX[r + 64][c8 * 8]) = V##2;                \
+        *reinterpret_cast<uint4 *>(&sX[r + 96][c8 * 8]) = V##3;                \
+        *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = V##4;                     \
+        *reinterpret_cast<uint4 *>(&sW[r + 32][c8 * 8]) = V##5;                \
+        *reinterpret_cast<uint4 *>(&sU[r][c8 * 8]) = V##6;                     \
+        *reinterpret_cast<uint4 *>(&sU[r + 32][c8 * 8]) = V##7;                \
+    } while (0)
+    uint4 a0, a1, a2, a3, a4, a5, a6, a7;
+    MOE_GEMM2_LOAD(a, 0);
 #pragma unroll 1
-    for (; c + 2 < NC; c += 2) {
-        MOE_GEMM2_STORE(ax0, ax1, ag0, ag1, au0, au1);
+    for (int c = 0; c < NC; ++c) {
+        MOE_GEMM2_STORE(a);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        MOE_GEMM2_LOAD(ax0, ax1, ag0, ag1, au0, au1, c + 2);
+        MOE_GEMM2_LOAD(a, min(c + 1, NC - 1));  // (the last chunk again at the end: unused)
         __builtin_amdgcn_sched_barrier(0);
-        gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
-        __syncthreads();
-        MOE_GEMM2_STORE(bx0, bx1, bg0, bg1, bu0, bu1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_GEMM2_LOAD(bx0, bx1, bg0, bg1, bu0, bu1, c + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
+        gemm2_mma(acc, sX, sW, sU, wm, wn, lane);
         __syncthreads();
     }
-    MOE_GEMM2_STORE(ax0, ax1, ag0, ag1, au0, au1);
-    __syncthreads();
-    gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
-    __syncthreads();
-    MOE_GEMM2_STORE(bx0, bx1, bg0, bg1, bu0, bu1);
-    __syncthreads();
-    gemm2_mma(accg, accu, sX, sW, sU, wm, wn, lane);
-    __syncthreads();
 }
 #undef MOE_GEMM2_LOAD
 #undef MOE_GEMM2_STORE
 
+// LDS of a projection workgroup: a pair of 64-token tiles x 64 rows.
 struct MfmaProjLds {
-    uint16_t sX[kTM][kRow];
+    uint16_t sX[2 * kTM][kRow];
     uint16_t sW[kTN][kRow];
     uint16_t sU[kTN][kRow];
-    uint32_t sMask[kTM][2];
-    uint32_t sAct[2];
-    int sTok[kTM];
-    int sList[kTN];
-    int sNact;
+    uint32_t sMask[2 * kTM][2];
+    uint32_t sAct[2][2];        // [token tile][word]
+    int sTok[2 * kTM];
+    int sList[2][kTN];
 };
 
 constexpr int kWdRow = kTC + 32;  // padded LDS row of the down tile (bf16): 320 bytes
@@ -291,19 +289,20 @@ __device__ __forceinline__ bf16x8_t lds_frag_tr(const uint16_t *tile, int ld, in
     return *reinterpret_cast<const bf16x8_t *>(v);
 }
 
-// Projection of one (item, 64-neuron tile); `b` and `nblocks` are this
-// workgroup's index among the MFMA workgroups and their count (a multiple of 8).
-// The gate and up products are computed together in one pass over the token
-// tile's hidden states (up for every row of the tile: at 32 or more tokens the
-// tile's union covers most rows, and a second pass over X for the active rows
-// alone read more bytes than it skipped); h keeps the sparse definition, with
-// an inactive (token, neuron) set to exactly 0 by a select, and only the
-// tile's active rows are stored, compacted, for the down projection.  Work
-// items run item-major (the neuron tiles of one token tile next to each other
-// on one XCD, sharing its hidden states in L2, then the expert's next token
-// tile, sharing the weight tiles).
+// Projection of one (item pair, 64-neuron tile): two adjacent 64-token tiles
+// of one expert (or its last tile alone), so each weight tile read serves 128
+// tokens.  `b` is this workgroup's index among the MFMA workgroups.  The gate
+// and up products are computed together in one pass over the tokens' hidden
+// states (up for every row of the tile: at 32 or more tokens the tile's union
+// covers most rows, and a second pass over X for the active rows alone read
+// more bytes than it skipped); h keeps the sparse definition, with an inactive
+// (token, neuron) set to exactly 0 by a select, and only each 64-token tile's
+// active rows are stored, compacted, for the down projection.  Work runs pair
+// major: the neuron tiles of one pair next to each other on one XCD (sharing
+// its hidden states in L2), then the expert's next pair (sharing the weight
+// tiles).
 template <int MODE>
-__device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds &S, int b, int nblocks)
+__device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds &S, int b)
 {
     auto &sX = S.sX;
     auto &sW = S.sW;
@@ -312,13 +311,13 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
     auto &sAct = S.sAct;
     auto &sTok = S.sTok;
     auto &sList = S.sList;
-    auto &sNact = S.sNact;
 
-    const int L = xcd_remap(b, nblocks);
-    if (L >= p.max_items * p.NT) return;
-    const int item = L / p.NT, nt = L - item * p.NT;
-    if (item >= p.hdr[1]) return;
-    const int code = p.items[item];
+    const int L = xcd_remap(b, p.hdr[2] * p.NT);
+    if (L < 0) return;
+    const int pi = L / p.NT, nt = L - pi * p.NT;
+    const int pcode = p.pairs[pi];
+    const int item0 = pcode >> 1, nblk = 1 + (pcode & 1);  // token tiles in the pair
+    const int code = p.items[item0];
     const int xe = code >> 16, tile = code & 0xffff;
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
@@ -326,99 +325,113 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
     if (n0 >= Ie) return;
     const int nrows = min(kTN, Ie - n0);  // 32 or 64
     const int n = p.counts[xe], off = p.offsets[xe];
-    const int m0 = tile * kTM, mt = min(kTM, n - m0);
+    const int m0 = tile * kTM, mt = min(nblk * kTM, n - m0);  // valid tokens of the pair
     const int H = p.H;
     const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * H;
     const uint16_t *Wg = (shared ? p.swg : p.wg) + mat + (size_t)n0 * H;
     const uint16_t *Wu = (shared ? p.swu : p.wu) + mat + (size_t)n0 * H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave & 1, wn = wave >> 1;  // wm: token tile of the pair
     const float tau = (MODE == MOE_SPARSE) ? p.tau[xe] : 0.f;
 
-    if (tid < kTM) sTok[tid] = tid < mt ? p.pair_tok[off + m0 + tid] : -1;
-    if (tid < 2) sAct[tid] = 0u;
-    if (tid < 2 * kTM) sMask[tid >> 1][tid & 1] = 0u;
+    if (tid < 2 * kTM) {
+        sTok[tid] = tid < mt ? p.pair_tok[off + m0 + tid] : -1;
+        sMask[tid][0] = sMask[tid][1] = 0u;
+    }
+    if (tid < 4) sAct[tid >> 1][tid & 1] = 0u;
     __syncthreads();
 
     // ---- gate and up ----------------------------------------------------------
-    f32x16_t accg = {}, accu = {};
-    gemm2_64x64(accg, accu, sX, sW, sU, p.x, sTok, Wg, Wu, nrows, H);
+    f32x16_t acc[2][2] = {};
+    gemm2_128x64(acc, sX, sW, sU, p.x, sTok, Wg, Wu, nrows, H);
 
-    // lane (r, lane) holds token m = 32 wm + 8 (r / 4) + 4 (lane / 32) + r % 4 and
-    // row nn = 32 wn + lane % 32 of both products
+    // acc[q][*] entry r of this lane: token m = 64 wm + 32 q + 8 (r / 4) +
+    // 4 (lane / 32) + r % 4 of the pair, row nn = 32 wn + lane % 32
     const int nn = 32 * wn + (lane & 31);
-    uint32_t actw = 0, mine = 0;  // mine: bit r = this lane's (m, nn) is active
+    uint32_t actw = 0, mine[2] = {0u, 0u};  // mine[q]: bit r = this lane's entry is active
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int mlo = 32 * wm + 8 * (r >> 2) + (r & 3);  // token of lanes 0..31; lanes 32..63 hold mlo + 4
-        const int m = mlo + 4 * (lane >> 5);
-        const float a = silu(accg[r]);
-        const bool valid = m < mt && nn < nrows;
-        const bool act = valid && (MODE == MOE_DENSE || !(fabsf(a) < tau));
-        accg[r] = a;
-        mine |= (uint32_t)act << r;
-        const uint64_t bb = __ballot(act);
-        if (lane == 0) {
-            sMask[mlo][wn] = (uint32_t)bb;
-            sMask[mlo + 4][wn] = (uint32_t)(bb >> 32);
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int mlo = 64 * wm + 32 * q + 8 * (r >> 2) + (r & 3);  // lanes 32..63 hold mlo + 4
+            const int m = mlo + 4 * (lane >> 5);
+            const float a = silu(acc[q][0][r]);
+            const bool valid = m < mt && nn < nrows;
+            const bool act = valid && (MODE == MOE_DENSE || !(fabsf(a) < tau));
+            acc[q][0][r] = a;
+            mine[q] |= (uint32_t)act << r;
+            const uint64_t bb = __ballot(act);
+            if (lane == 0) {
+                sMask[mlo][wn] = (uint32_t)bb;
+                sMask[mlo + 4][wn] = (uint32_t)(bb >> 32);
+            }
+            actw |= (uint32_t)bb | (uint32_t)(bb >> 32);
         }
-        actw |= (uint32_t)bb | (uint32_t)(bb >> 32);
-    }
-    if (lane == 0 && actw) atomicOr(&sAct[wn], actw);
+    if (lane == 0 && actw) atomicOr(&sAct[wm][wn], actw);
     __syncthreads();
 
-    // ---- masks, union, active rows ------------------------------------------
-    const int blk = item * p.NT + nt;
-    if (p.mask_bits && tid < 2 * kTM) {
-        const int m = tid >> 1, w = tid & 1;
+    // ---- masks, union, active rows of each token tile -------------------------
+    if (p.mask_bits) {
+        const int m = tid >> 1, w = tid & 1;  // tid < 256 = 2 x 128
         if (m < mt && 32 * w < nrows) {
             const int pr = off + m0 + m;
             const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
             p.mask_bits[row * p.W + (n0 >> 5) + w] = sMask[m][w];
         }
-    }
-    if (p.mask_bits && nt == 0 && tid < kTM && tid < mt) {
-        const int pr = off + m0 + tid;
-        const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
-        for (int wd = Ie / 32; wd < p.W; ++wd) p.mask_bits[row * p.W + wd] = 0u;
+        if (nt == 0 && tid < mt) {
+            const int pr = off + m0 + tid;
+            const size_t row = (size_t)p.pair_tok[pr] * p.slots + p.pair_slot[pr];
+            for (int wd = Ie / 32; wd < p.W; ++wd) p.mask_bits[row * p.W + wd] = 0u;
+        }
     }
     if (tid == 0) {
-        if (sAct[0]) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5)], sAct[0]);
-        if (nrows > 32 && sAct[1]) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5) + 1], sAct[1]);
+        const uint32_t u0 = sAct[0][0] | sAct[1][0], u1 = sAct[0][1] | sAct[1][1];
+        if (u0) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5)], u0);
+        if (nrows > 32 && u1) atomicOr(&p.union_words[(size_t)xe * p.W + (n0 >> 5) + 1], u1);
     }
-    const uint64_t act64 = (uint64_t)sAct[0] | ((uint64_t)sAct[1] << 32);
-    const int nact = __popcll(act64);
-    if (wave == 0) {
-        const bool bit = (act64 >> lane) & 1ull;
-        if (bit) sList[__popcll(act64 & lanemask_lt())] = lane;
+    if (wave < nblk) {  // wavefront j lists token tile j's active rows
+        const uint64_t a64 = (uint64_t)sAct[wave][0] | ((uint64_t)sAct[wave][1] << 32);
+        if ((a64 >> lane) & 1ull) sList[wave][__popcll(a64 & lanemask_lt())] = lane;
     }
     __syncthreads();
-    if (tid == 0) p.nact[blk] = nact;
-    if (tid < nact) p.list[(size_t)blk * kTN + tid] = (uint8_t)sList[tid];
-    if (nact == 0) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (j >= nblk) break;
+        const int blk = (item0 + j) * p.NT + nt;
+        const int na = __popc(sAct[j][0]) + __popc(sAct[j][1]);
+        if (tid == 0) p.nact[blk] = na;
+        if (tid < na) p.list[(size_t)blk * kTN + tid] = (uint8_t)sList[j][tid];
+    }
+    if (wm >= nblk) return;  // (no second token tile)
 
-    // ---- h of the active rows, compacted -------------------------------------
-    // active row nn goes to column (its rank among the active rows, < nact);
-    // the lane of row nn >= nact also zeroes column nn, so every column of the
-    // block is written (the down product reads zeros past nact)
+    // ---- h of token tile wm's active rows, compacted ---------------------------
+    // active row nn goes to column (its rank among the tile's active rows,
+    // < nact); the lane of row nn >= nact also zeroes column nn, so every
+    // column of the block is written (the down product reads zeros past nact)
+    const uint64_t act64 = (uint64_t)sAct[wm][0] | ((uint64_t)sAct[wm][1] << 32);
+    const int nact = __popcll(act64);
+    if (nact == 0) return;
     const bool row_act = (act64 >> nn) & 1ull;
     const int col = __popcll(act64 & ((1ull << nn) - 1ull));
+    const int blk = (item0 + wm) * p.NT + nt;
     uint16_t *hhi = p.hhi + (size_t)blk * kTM * kTN;
     uint16_t *hlo = p.hlo + (size_t)blk * kTM * kTN;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int m = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row_act) {
-            const float hv = ((mine >> r) & 1u) ? accg[r] * accu[r] : 0.f;  // a select: inactive adds exactly 0
-            const uint16_t hi = bf16_rne(hv);
-            hhi[m * kTN + col] = hi;
-            hlo[m * kTN + col] = bf16_rne(hv - bf16_to_f32(hi));
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 32 * q + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // token within the tile
+            if (row_act) {
+                const float hv = ((mine[q] >> r) & 1u) ? acc[q][0][r] * acc[q][1][r] : 0.f;  // a select
+                const uint16_t hi = bf16_rne(hv);
+                hhi[m * kTN + col] = hi;
+                hlo[m * kTN + col] = bf16_rne(hv - bf16_to_f32(hi));
+            }
+            if (nn >= nact) {
+                hhi[m * kTN + nn] = 0;
+                hlo[m * kTN + nn] = 0;
+            }
         }
-        if (nn >= nact) {
-            hhi[m * kTN + nn] = 0;
-            hlo[m * kTN + nn] = 0;
-        }
-    }
 }
 
 // Down projection of one (item, 128-column tile): O = sum over the expert's
@@ -430,7 +443,7 @@ __device__ __forceinline__ void mfma_proj_body(const MfmaParams &p, MfmaProjLds 
 // last active row, and h columns past them are zero: every load is
 // unconditional.
 template <int MODE>
-__device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds &S, int b, int nblocks)
+__device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds &S, int b)
 {
     auto &sHhi = S.sHhi;
     auto &sHlo = S.sHlo;
@@ -440,10 +453,10 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     auto &s_wpre = S.s_wpre;
 
     const int nct = p.H / kTC;
-    const int L = xcd_remap(b, nblocks);
-    if (L >= p.max_items * nct) return;
-    const int ct = L / p.max_items, item = L - ct * p.max_items;
-    if (item >= p.hdr[1]) return;
+    const int nitems = p.hdr[1];
+    const int L = xcd_remap(b, nitems * nct);
+    if (L < 0) return;
+    const int ct = L / nitems, item = L - ct * nitems;
     const int code = p.items[item];
     const int xe = code >> 16, tile = code & 0xffff;
     const bool shared = xe >= p.E;

@@ -47,11 +47,12 @@ struct Plan {
     int nm;          // pair-count threshold (INT_MAX when the path is off)
     int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
     int max_items;   // upper bound on (expert, 64-token tile) work items
+    int max_pairs;   // upper bound on pairs of them (the MFMA projection's items)
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
     size_t off_taus;
-    size_t off_items, off_nact, off_list, off_hhi, off_hlo;
+    size_t off_items, off_pairs, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
 };
 
@@ -79,6 +80,7 @@ struct GroupParams {
     int W;
     int nm;               // MFMA pair-count threshold
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
+    int32_t *pairs;       // [max_pairs] (first item << 1 | has a second) for the MFMA projection
 };
 
 struct ProjParams {
@@ -125,7 +127,7 @@ struct CombineParams {
 struct MfmaParams {
     const uint16_t *x, *wg, *wu, *wd, *swg, *swu, *swd;
     const float *tau;
-    const int32_t *hdr, *counts, *offsets, *items, *pair_tok, *pair_slot;
+    const int32_t *hdr, *counts, *offsets, *items, *pairs, *pair_tok, *pair_slot;
     uint16_t *hhi, *hlo;  // compacted h per (item, neuron tile): [64 tokens][64] bf16 hi / lo
     int32_t *nact;        // active rows per (item, neuron tile)
     uint8_t *list;        // their offsets within the tile, ascending
@@ -133,7 +135,7 @@ struct MfmaParams {
     float *partial;       // as DownParams (piece 0 only)
     int32_t *npc;         // as DownParams
     int32_t *union_idx, *union_cnt;
-    int H, E, I, Is, S, W, Imax, slots, NT, max_items, NCT;
+    int H, E, I, Is, S, W, Imax, slots, NT, max_items, max_pairs, NCT;
 };
 
 struct SelectParams {

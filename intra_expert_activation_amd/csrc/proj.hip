@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams m
         proj_gemv<BF16, 4, NSW, TTMAX, MODE>(p, S.gemv, blockIdx.x);
     } else {
         if constexpr (MODE != kModeScore)
-            mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks, gridDim.x - gemv_blocks);
+            mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks);
     }
 }
 
@@ -330,7 +330,7 @@ static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const Mfma
     if constexpr (std::is_same<Tr, BF16>::value && NW == 4) {
         if (mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
             const int gemv = round8((long long)pl.max_touched * pl.C);
-            const int grid = gemv + round8((long long)pl.max_items * pl.NT);
+            const int grid = gemv + round8((long long)pl.max_pairs * pl.NT);
             hipLaunchKernelGGL((k_proj_bf16<NSW, TT, MODE>), dim3(grid), dim3(256), 0, st, pp, mp, gemv);
             return hipGetLastError();
         }

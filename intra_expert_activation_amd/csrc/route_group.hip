@@ -256,14 +256,36 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             const int o = __shfl_up(iincl, s, kWave);
             if (lane >= s) iincl += o;
         }
-        int ipos = iincl - tiles;
+        // and the projection's item pairs (two adjacent token tiles of one
+        // expert, or its last tile alone): (first item index << 1) | has second
+        int npairs = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int e = lane * kPer + i;
-            if (e < EX && loc[i] >= p.nm)
-                for (int tl = 0; tl < (loc[i] + kMfmaTokens - 1) / kMfmaTokens; ++tl) p.items[ipos++] = (e << 16) | tl;
+            if (e < EX && loc[i] >= p.nm) npairs += ((loc[i] + kMfmaTokens - 1) / kMfmaTokens + 1) / 2;
         }
-        if (lane == kWave - 1) p.hdr[1] = iincl;
+        int pincl = npairs;
+#pragma unroll
+        for (int s = 1; s < kWave; s <<= 1) {
+            const int o = __shfl_up(pincl, s, kWave);
+            if (lane >= s) pincl += o;
+        }
+        int ipos = iincl - tiles, ppos = pincl - npairs;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX && loc[i] >= p.nm) {
+                const int nt = (loc[i] + kMfmaTokens - 1) / kMfmaTokens;
+                for (int tl = 0; tl < nt; ++tl) {
+                    if ((tl & 1) == 0) p.pairs[ppos++] = (ipos << 1) | (tl + 1 < nt ? 1 : 0);
+                    p.items[ipos++] = (e << 16) | tl;
+                }
+            }
+        }
+        if (lane == kWave - 1) {
+            p.hdr[1] = iincl;
+            p.hdr[2] = pincl;
+        }
     }
     __syncthreads();
     // union words of the MFMA experts are built with atomic ORs: clear them
