@@ -456,7 +456,7 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     const int nitems = p.hdr[1];
     const int L = xcd_remap(b, nitems * nct);
     if (L < 0) return;
-    const int ct = L / nitems, item = L - ct * nitems;
+    const int item = L / nct, ct = L - item * nct;  // item-major: the item's h tiles stay in L2 across its column tiles
     const int code = p.items[item];
     const int xe = code >> 16, tile = code & 0xffff;
     const bool shared = xe >= p.E;
