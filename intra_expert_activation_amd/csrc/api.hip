@@ -132,6 +132,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     const size_t blocks = (size_t)p->max_items * p->NT;
     p->off_items = take((size_t)p->max_items * 4);
     p->off_pairs = take((size_t)p->max_pairs * 4);
+    p->off_blockcnt = take((size_t)((p->A + kGroupBlock - 1) / kGroupBlock) * p->E * 4);
     p->off_nact = take(blocks * 4);
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);
@@ -250,6 +251,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
     gp.pairs = ws_at<int32_t>(ws, pl.off_pairs);
+    gp.blockcnt = ws_at<int32_t>(ws, pl.off_blockcnt);
     if (launch_route_group(a->router_logits, pl.renorm, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
@@ -341,6 +343,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr; gp.pairs = nullptr;
+    gp.blockcnt = ws_at<int32_t>(workspace, pl.off_blockcnt);
     if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};

@@ -16,6 +16,7 @@ constexpr int kMaxK = 32;
 constexpr int kMaxRows = 16384;    // I, I_shared
 constexpr int kMaxRowsPerChunk = 256;
 constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
+constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
 constexpr int kMfmaMinPairs = 32;  // default pair-count threshold of the MFMA path
 
 // ---------------------------------------------------------------------------
@@ -52,7 +53,7 @@ struct Plan {
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
     size_t off_taus;
-    size_t off_items, off_pairs, off_nact, off_list, off_hhi, off_hlo;
+    size_t off_items, off_pairs, off_blockcnt, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
 };
 
@@ -81,6 +82,7 @@ struct GroupParams {
     int nm;               // MFMA pair-count threshold
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
     int32_t *pairs;       // [max_pairs] (first item << 1 | has a second) for the MFMA projection
+    int32_t *blockcnt;    // [ceil(A / kGroupBlock), E] per-block expert counts (large batches), or null
 };
 
 struct ProjParams {

@@ -134,10 +134,18 @@ __device__ __forceinline__ void load_id_batch(const int32_t *ids, int b0, int a_
     for (int j = 0; j < kIdBatch; ++j) ev[j] = ids[min(b0 + j * kWave + lane, a_end - 1)];
 }
 
-__device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *ids)
+// Groups the routed pairs [rb, re) (the whole batch, or one block of it).
+// With blockcnt (per-block expert counts of nblk blocks of kGroupBlock pairs,
+// this being block myblk), an expert's pairs from earlier blocks come first;
+// without it the range is the whole batch.  Only the writer workgroup stores
+// the per-expert metadata (counts, offsets, touched lists, MFMA work items)
+// and the shared experts' pairs; every workgroup derives the same offsets.
+__device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *ids, int rb, int re,
+                                           const int32_t *blockcnt, int nblk, int myblk, bool writer)
 {
     __shared__ int s_cnt[kGroupWaves][kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_before[kMaxExperts];  // this expert's pairs in earlier blocks
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -146,10 +154,10 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     for (int i = tid; i < kGroupWaves * kMaxExperts; i += blockDim.x) (&s_cnt[0][0])[i] = 0;
     __syncthreads();
 
-    const int chunks = (p.A + kWave - 1) / kWave;
+    const int chunks = (re - rb + kWave - 1) / kWave;
     const int per_wave = (chunks + kGroupWaves - 1) / kGroupWaves;
-    const int a_begin = wv * per_wave * kWave;
-    const int a_end = min(p.A, (wv + 1) * per_wave * kWave);
+    const int a_begin = rb + wv * per_wave * kWave;
+    const int a_end = min(re, rb + (wv + 1) * per_wave * kWave);
 
     // pass 1: per-wavefront counts (the ids of kIdBatch chunks are loaded at
     // once: one memory latency per batch instead of one per chunk)
@@ -170,17 +178,27 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
 
     // per-expert totals; s_cnt becomes the per-wavefront base inside the expert
     for (int e = tid; e < EX; e += blockDim.x) {
-        int run = 0;
+        int run = 0, before = 0;
         if (e < p.E) {
             for (int w2 = 0; w2 < kGroupWaves; ++w2) {
                 const int c = s_cnt[w2][e];
                 s_cnt[w2][e] = run;
                 run += c;
             }
+            if (blockcnt) {  // the whole batch's count, and the earlier blocks' share
+                int tot = 0;
+                for (int b = 0; b < nblk; ++b) {
+                    const int c = blockcnt[(size_t)b * p.E + e];
+                    tot += c;
+                    before += b < myblk ? c : 0;
+                }
+                run = tot;
+            }
         } else {
             run = p.T;  // a shared expert serves every token
         }
         s_off[e] = run;  // total for now
+        s_before[e] = before;
     }
     __syncthreads();
     if (wv == 0) {
@@ -207,18 +225,21 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         for (int i = 0; i < kPer; ++i) {
             const int e = lane * kPer + i;
             if (e < EX) {
-                p.counts[e] = loc[i];
-                p.offsets[e] = run;
+                if (writer) {
+                    p.counts[e] = loc[i];
+                    p.offsets[e] = run;
+                    if (p.ucount) p.ucount[e] = 0;
+                }
                 s_off[e] = run;
-                if (p.ucount) p.ucount[e] = 0;
             }
             run += loc[i];
             ntouched_before += (e < EX && loc[i] > 0) ? 1 : 0;
         }
         if (lane == kWave - 1) {
-            p.offsets[EX] = run;
+            if (writer) p.offsets[EX] = run;
             s_off[EX] = run;
         }
+      if (writer) {
         // touched experts, ascending: exclusive prefix of per-lane touched counts
         int tincl = ntouched_before;
 #pragma unroll
@@ -286,10 +307,11 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             p.hdr[1] = iincl;
             p.hdr[2] = pincl;
         }
+      }
     }
     __syncthreads();
     // union words of the MFMA experts are built with atomic ORs: clear them
-    if (p.union_words)
+    if (writer && p.union_words)
         for (int i = tid; i < EX * p.W; i += blockDim.x) {
             const int e = i / p.W;
             if (s_off[e + 1] - s_off[e] >= p.nm) p.union_words[i] = 0u;
@@ -313,7 +335,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             old = __shfl(old, leader, kWave);
             if (valid) {
                 const int rank = __popcll(peers & lanemask_lt());
-                const int pos = s_off[e] + old + rank;
+                const int pos = s_off[e] + s_before[e] + old + rank;
                 const int t = a / p.K, k = a - t * p.K;
                 p.pair_tok[pos] = t;
                 p.pair_slot[pos] = k;
@@ -321,6 +343,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         }
     }
     // shared experts: pair A + s*T + t
+    if (writer)
     for (int i = tid; i < p.S * p.T; i += blockDim.x) {
         const int s = i / p.T, t = i - s * p.T;
         const int pos = p.A + i;
@@ -329,7 +352,29 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     }
 }
 
-__global__ __launch_bounds__(1024) void k_group(GroupParams p) { group_body(p, p.ids); }
+__global__ __launch_bounds__(1024) void k_group(GroupParams p) { group_body(p, p.ids, 0, p.A, nullptr, 0, 0, true); }
+
+// Large batches: the grouping over blocks of kGroupBlock pairs, one workgroup
+// each.  k_group_count stores each block's per-expert counts; k_group_scatter
+// places each block's pairs after the same expert's pairs of earlier blocks
+// (the same stable order as one workgroup over the whole batch), and its
+// block 0 stores the per-expert metadata.
+__global__ __launch_bounds__(256) void k_group_count(GroupParams p)
+{
+    __shared__ int s_h[kMaxExperts];
+    for (int e = threadIdx.x; e < p.E; e += blockDim.x) s_h[e] = 0;
+    __syncthreads();
+    const int rb = blockIdx.x * kGroupBlock, re = min(p.A, rb + kGroupBlock);
+    for (int a = rb + threadIdx.x; a < re; a += blockDim.x) atomicAdd(&s_h[p.ids[a]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < p.E; e += blockDim.x) p.blockcnt[(size_t)blockIdx.x * p.E + e] = s_h[e];
+}
+
+__global__ __launch_bounds__(1024) void k_group_scatter(GroupParams p)
+{
+    const int b = blockIdx.x;
+    group_body(p, p.ids, b * kGroupBlock, min(p.A, (b + 1) * kGroupBlock), p.blockcnt, gridDim.x, b, b == 0);
+}
 
 // Routing (many workgroups, one wavefront per token) then grouping (one
 // workgroup).  Routing inside the grouping workgroup was slower at every
@@ -342,7 +387,13 @@ hipError_t launch_route_group(const float *logits, int renorm, int32_t *ids, flo
     if (gp.T <= 0) return hipSuccess;
     const hipError_t e = launch_route(logits, gp.T, gp.E, gp.K, renorm, ids, w, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupWaves * kWave), 0, stream, gp);
+    if (gp.A > kGroupBlock && gp.blockcnt) {
+        const int nb = (gp.A + kGroupBlock - 1) / kGroupBlock;
+        hipLaunchKernelGGL(k_group_count, dim3(nb), dim3(256), 0, stream, gp);
+        hipLaunchKernelGGL(k_group_scatter, dim3(nb), dim3(kGroupWaves * kWave), 0, stream, gp);
+    } else {
+        hipLaunchKernelGGL(k_group, dim3(1), dim3(kGroupWaves * kWave), 0, stream, gp);
+    }
     return hipGetLastError();
 }
 
