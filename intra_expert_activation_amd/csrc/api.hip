@@ -80,14 +80,18 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // KMAX pieces, whose partial sums the combine adds in order.
     p->NCT = (p->H + 1023) / 1024;
     // KMAX - 1 >= Imax / kDownChunk, so shares of kDownChunk rows never cut a
-    // group into more than KMAX pieces
+    // group into more than KMAX pieces.  Shares are at least umax / (KMAX - 1)
+    // rows, so a small KMAX idles workgroups when few wide experts hold all
+    // the work: one piece per 512 rows of I keeps shares down to ~256 rows
+    // there, at a partial-sum cost of a few percent of the weight bytes.
     p->KMAX = 8;
+    if ((p->Imax + 511) / 512 + 1 > p->KMAX) p->KMAX = (p->Imax + 511) / 512 + 1;
     if ((p->Imax + kDownChunk - 1) / kDownChunk + 1 > p->KMAX) p->KMAX = (p->Imax + kDownChunk - 1) / kDownChunk + 1;
-    {
-        long long gd = (long long)(p->max_touched > 0 ? p->max_touched : 1) * p->NCT * 4;
-        if (gd > 1024) gd = 1024;
-        p->GD = (int)((gd + 7) / 8 * 8);
-    }
+    // every resident workgroup takes a share (shares never go below
+    // kMinShare rows, so small batches leave the rest idle); sizing GD by the
+    // number of touched experts starved layers of few, wide experts (8 experts
+    // x 14336 rows: 128 workgroups, 1.1 TB/s)
+    p->GD = 1024;
 
     // MFMA path: bf16 experts with at least kMfmaMinPairs pairs.  A routed
     // expert has at most T pairs, so with T below the threshold it is off.

@@ -302,21 +302,22 @@ __global__ __launch_bounds__(NW * 64) void k_proj(ProjParams p)
     proj_gemv<Tr, NW, NSW, TTMAX, MODE>(p, L, blockIdx.x);
 }
 
-// bf16 layers with 256-thread GEMV workgroups: one launch runs the GEMV
-// chunks (workgroups [0, gemv_blocks)) and the MFMA tiles (the rest).
-// gemv_blocks is a multiple of 8, so the MFMA workgroups keep their XCD order.
+// bf16 layers with 256-thread GEMV workgroups: one launch runs the MFMA tiles
+// (workgroups [0, mfma_blocks)) and the GEMV chunks (the rest).  The MFMA
+// tiles come first so that their arithmetic overlaps the GEMV chunks' weight
+// streaming instead of trailing it; mfma_blocks is a multiple of 8, so they
+// keep their XCD order.
 template <int NSW, int TTMAX, int MODE>
-__global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams mp, int gemv_blocks)
+__global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams mp, int mfma_blocks)
 {
     __shared__ union {
         ProjLds<4, TTMAX> gemv;
         MfmaProjLds mfma;
     } S;
-    if ((int)blockIdx.x < gemv_blocks) {
-        proj_gemv<BF16, 4, NSW, TTMAX, MODE>(p, S.gemv, blockIdx.x);
+    if ((int)blockIdx.x >= mfma_blocks) {
+        proj_gemv<BF16, 4, NSW, TTMAX, MODE>(p, S.gemv, blockIdx.x - mfma_blocks);
     } else {
-        if constexpr (MODE != kModeScore)
-            mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x - gemv_blocks);
+        if constexpr (MODE != kModeScore) mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x);
     }
 }
 
@@ -329,9 +330,9 @@ static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const Mfma
     const bool mfma = MODE != kModeScore && pl.use_mfma;
     if constexpr (std::is_same<Tr, BF16>::value && NW == 4) {
         if (mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
-            const int gemv = round8((long long)pl.max_touched * pl.C);
-            const int grid = gemv + round8((long long)pl.max_pairs * pl.NT);
-            hipLaunchKernelGGL((k_proj_bf16<NSW, TT, MODE>), dim3(grid), dim3(256), 0, st, pp, mp, gemv);
+            const int mfma_blocks = round8((long long)pl.max_pairs * pl.NT);
+            const int grid = mfma_blocks + pl.max_touched * pl.C;
+            hipLaunchKernelGGL((k_proj_bf16<NSW, TT, MODE>), dim3(grid), dim3(256), 0, st, pp, mp, mfma_blocks);
             return hipGetLastError();
         }
     }
