@@ -173,6 +173,7 @@ def test_mfma_and_gemv_paths_agree_at_threshold():
     ((("E", 300), ("K", 3), ("I", 64)), 50),                        # many experts
     ((("H", 512), ("E", 6), ("I", 96), ("K", 2)), 7),               # H = 512 (one vector per lane)
     ((("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 3),              # H = 8192 (16 vectors per lane)
+    ((("H", 512), ("E", 2), ("I", 16384), ("K", 1)), 5),            # I = 16384 (the largest), KMAX pieces
 ])
 def test_edge_shapes_bf16(over, T):
     c, L = cached_layer(2, over)
