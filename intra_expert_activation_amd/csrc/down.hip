@@ -78,23 +78,55 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 // to list[0 .. b - a).  Lane l holds words l, l + 64, ...; the neurons are
 // visited 64 at a time (lane i takes neuron 64 kb + i), and a ballot with a
 // masked popcount gives each set bit its position, so the list comes out in
-// ascending order without a per-bit loop.  Stops once position b is reached.
+// ascending order without a per-bit loop.  A prefix sum of the words'
+// popcounts finds the word holding position a, so the visit starts there
+// (not at word 0) and stops once position b is reached.
 constexpr int kMaxWordsPerLane = kMaxRows / 32 / kWave;  // 8
 
-// The same for nw <= 64 with lane l's word already loaded.
-__device__ __forceinline__ void wave_union_list_1(uint32_t word, int nw, int a, int b, uint16_t *list, int lane)
+// Inclusive prefix sum over the 64 lanes: DPP row shifts within each row of
+// 16 lanes (out-of-row sources read 0), then row broadcasts of lanes 15 and
+// 31 into the rows after them.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x)
 {
-    const uint64_t below = lanemask_lt();
-    int base = 0;
-    for (int kk = 0; 2 * kk < nw && base < b; ++kk) {
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)word, 2 * kk);
-        const uint32_t hi = 2 * kk + 1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)word, 2 * kk + 1) : 0u;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// The ballot walk over word pairs [2 kk0, ...) of one register of words,
+// starting at union position base; returns the position after the walk.
+__device__ __forceinline__ int union_walk(uint32_t words, int wbase, int nw, int kk0, int base, int a, int b,
+                                          uint16_t *list, int lane, uint64_t below)
+{
+    for (int kk = kk0; kk < kWave / 2; ++kk) {
+        const int w0 = wbase + 2 * kk;  // the block's first word
+        if (w0 >= nw || base >= b) break;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)words, 2 * kk);
+        const uint32_t hi = w0 + 1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)words, 2 * kk + 1) : 0u;
         const bool bit = (((lane < 32) ? lo : hi) >> (lane & 31)) & 1u;
         const uint64_t m = __ballot(bit);
         const int pos = base + __popcll(m & below);
-        if (bit && pos >= a && pos < b) list[pos - a] = (uint16_t)(64 * kk + lane);
+        if (bit && pos >= a && pos < b) list[pos - a] = (uint16_t)(w0 * 32 + lane);
         base += __popcll(m);
     }
+    return base;
+}
+
+// The same for nw <= 64 with lane l's word already loaded (0 past nw).
+__device__ __forceinline__ void wave_union_list_1(uint32_t word, int nw, int a, int b, uint16_t *list, int lane)
+{
+    const int c = __popc(word);
+    const int ex = wave_incl_scan_dpp(c) - c;  // set bits before this word
+    // the last word whose prefix is <= a holds position a (a < b <= total)
+    const uint64_t le = __ballot(lane < nw && ex <= a);
+    const int w0 = 63 - __clzll((long long)le);
+    const int kk0 = w0 >> 1;
+    const int base = __builtin_amdgcn_readlane(ex, 2 * kk0);
+    union_walk(word, 0, nw, kk0, base, a, b, list, lane, lanemask_lt());
     wave_lds_sync();
 }
 
@@ -102,24 +134,37 @@ __device__ __forceinline__ void wave_union_list(const uint32_t *uw, int nw, int 
                                                 int lane)
 {
     uint32_t words[kMaxWordsPerLane];
+    int ex[kMaxWordsPerLane];
 #pragma unroll
     for (int r = 0; r < kMaxWordsPerLane; ++r) words[r] = (r * kWave + lane < nw) ? uw[r * kWave + lane] : 0u;
-    const uint64_t below = lanemask_lt();
-    int base = 0;  // union position of the current block's first set bit
+    int run = 0;
 #pragma unroll
     for (int r = 0; r < kMaxWordsPerLane; ++r) {
-        if (r * kWave >= nw || base >= b) break;
-        for (int kk = 0; kk < kWave / 2; ++kk) {
-            const int w0 = r * kWave + 2 * kk;  // the block's first word
-            if (w0 >= nw || base >= b) break;
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)words[r], 2 * kk);
-            const uint32_t hi = w0 + 1 < nw ? (uint32_t)__builtin_amdgcn_readlane((int)words[r], 2 * kk + 1) : 0u;
-            const bool bit = (((lane < 32) ? lo : hi) >> (lane & 31)) & 1u;
-            const uint64_t m = __ballot(bit);
-            const int pos = base + __popcll(m & below);
-            if (bit && pos >= a && pos < b) list[pos - a] = (uint16_t)(w0 * 32 + lane);
-            base += __popcll(m);
+        const int c = __popc(words[r]);
+        const int incl = wave_incl_scan_dpp(c);
+        ex[r] = run + incl - c;
+        run += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    const uint64_t below = lanemask_lt();
+    int base = -1;  // set when the walk has started
+#pragma unroll
+    for (int r = 0; r < kMaxWordsPerLane; ++r) {
+        if (r * kWave >= nw) break;
+        int kk0 = 0;
+        if (base < 0) {
+            // does position a lie in this register's words (or before the next's)?
+            const uint64_t le = __ballot(r * kWave + lane < nw && ex[r] <= a);
+            const int nr = min(kWave, nw - r * kWave);  // words in this register
+            if (le == 0) continue;  // (cannot happen for r = 0)
+            const int wl = 63 - __clzll((long long)le);
+            const bool later = r + 1 < kMaxWordsPerLane && (r + 1) * kWave < nw &&
+                               __builtin_amdgcn_readfirstlane(ex[r + 1 < kMaxWordsPerLane ? r + 1 : r]) <= a;
+            if (wl == nr - 1 && later) continue;  // a lies in a later register's words
+            kk0 = wl >> 1;
+            base = __builtin_amdgcn_readlane(ex[r], 2 * kk0);
         }
+        if (base >= b) break;
+        base = union_walk(words[r], r * kWave, nw, kk0, base, a, b, list, lane, below);
     }
     wave_lds_sync();
 }
