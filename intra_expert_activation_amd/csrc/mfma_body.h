@@ -71,97 +71,6 @@ __device__ __forceinline__ bf16x8_t lds_frag(const uint16_t *row_base, int k)
     return *reinterpret_cast<const bf16x8_t *>(row_base + k);
 }
 
-// One 64 x 64 x H product C += X[rows sTok] * W[rows given by wrow(r)]^T with the
-// 2x2 wavefront layout; `active` gates the MFMAs of this wavefront (all
-// wavefronts always load, store and synchronise).  Token entries below 0 and
-// rows that wrow() reports as below 0 are padding: they load row 0 of their
-// operand instead (every load is unconditional, so the compiler's waits cover
-// exactly one chunk) and only feed accumulator entries that are never used.
-// K advances in chunks of kKC staged through LDS; two chunks are in flight in
-// registers while the MFMAs consume the one in LDS.
-// Loads of chunk c (this thread's four 16-byte pieces) and their LDS stores.
-#define MOE_GEMM_LOAD(X0, X1, W0, W1, c)                                  \
-    do {                                                                  \
-        X0 = *reinterpret_cast<const uint4 *>(xp0 + (c) * kKC);           \
-        X1 = *reinterpret_cast<const uint4 *>(xp1 + (c) * kKC);           \
-        W0 = *reinterpret_cast<const uint4 *>(wp0 + (c) * kKC);           \
-        W1 = *reinterpret_cast<const uint4 *>(wp1 + (c) * kKC);           \
-    } while (0)
-#define MOE_GEMM_STORE(X0, X1, W0, W1)                                    \
-    do {                                                                  \
-        *reinterpret_cast<uint4 *>(&sX[r][c8 * 8]) = X0;                  \
-        *reinterpret_cast<uint4 *>(&sX[r + 32][c8 * 8]) = X1;             \
-        *reinterpret_cast<uint4 *>(&sW[r][c8 * 8]) = W0;                  \
-        *reinterpret_cast<uint4 *>(&sW[r + 32][c8 * 8]) = W1;             \
-    } while (0)
-
-__device__ __forceinline__ void gemm_mma(f32x16_t &acc, uint16_t (*sX)[kRow], uint16_t (*sW)[kRow], int wm, int wn,
-                                         int lane, bool active)
-{
-    if (!active) return;
-#pragma unroll
-    for (int s = 0; s < kKC / 16; ++s) {
-        const int k = 16 * s + 8 * (lane >> 5);
-        const bf16x8_t a = lds_frag(sX[32 * wm + (lane & 31)], k);
-        const bf16x8_t b = lds_frag(sW[32 * wn + (lane & 31)], k);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-    }
-}
-
-template <class WRow>
-__device__ __forceinline__ void gemm_64x64(f32x16_t &acc, uint16_t (*sX)[kRow], uint16_t (*sW)[kRow],
-                                           const uint16_t *X, const int *sTok, const uint16_t *W, WRow wrow,
-                                           int H, bool active)
-{
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    // this thread's two 16-byte pieces of each chunk: rows r and r + 32
-    const int r = tid >> 3, c8 = tid & 7;
-    const int t0 = sTok[r], t1 = sTok[r + 32];
-    const int w0 = wrow(r), w1 = wrow(r + 32);
-    const uint16_t *xp0 = X + (size_t)(t0 >= 0 ? t0 : 0) * H + c8 * 8;
-    const uint16_t *xp1 = X + (size_t)(t1 >= 0 ? t1 : 0) * H + c8 * 8;
-    const uint16_t *wp0 = W + (size_t)(w0 >= 0 ? w0 : 0) * H + c8 * 8;
-    const uint16_t *wp1 = W + (size_t)(w1 >= 0 ? w1 : 0) * H + c8 * 8;
-    // chunk c: store it (its loads were issued two chunks earlier), issue chunk
-    // c + 2, multiply, and let every wavefront finish reading LDS before the
-    // next store.  NC = H / kKC is even and at least 8.
-    const int NC = H / kKC;
-    uint4 ax0, ax1, aw0, aw1, bx0, bx1, bw0, bw1;
-    MOE_GEMM_LOAD(ax0, ax1, aw0, aw1, 0);
-    __builtin_amdgcn_sched_barrier(0);  // chunk 0's loads strictly before chunk 1's
-    MOE_GEMM_LOAD(bx0, bx1, bw0, bw1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    int c = 0;
-#pragma unroll 1
-    for (; c + 2 < NC; c += 2) {
-        MOE_GEMM_STORE(ax0, ax1, aw0, aw1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_GEMM_LOAD(ax0, ax1, aw0, aw1, c + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        gemm_mma(acc, sX, sW, wm, wn, lane, active);
-        __syncthreads();
-        MOE_GEMM_STORE(bx0, bx1, bw0, bw1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_GEMM_LOAD(bx0, bx1, bw0, bw1, c + 3);  // c + 2 < NC with c, NC even: c + 3 < NC
-        __builtin_amdgcn_sched_barrier(0);
-        gemm_mma(acc, sX, sW, wm, wn, lane, active);
-        __syncthreads();
-    }
-    // c = NC - 2: chunks NC - 2 (a) and NC - 1 (b) are in flight
-    MOE_GEMM_STORE(ax0, ax1, aw0, aw1);
-    __syncthreads();
-    gemm_mma(acc, sX, sW, wm, wn, lane, active);
-    __syncthreads();
-    MOE_GEMM_STORE(bx0, bx1, bw0, bw1);
-    __syncthreads();
-    gemm_mma(acc, sX, sW, wm, wn, lane, active);
-    __syncthreads();
-}
-#undef MOE_GEMM_LOAD
-#undef MOE_GEMM_STORE
 
 __device__ __forceinline__ void gemm2_mma(f32x16_t (&acc)[2][2], uint16_t (*sX)[kRow], uint16_t (*sW)[kRow],
                                           uint16_t (*sU)[kRow], int wm, int wn, int lane)
