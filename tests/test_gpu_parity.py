@@ -102,6 +102,21 @@ def test_deepseek_shared(T, q):
     print(f"T={T} q={q} err={s['err']:.2e} band={s['band']} flips={s['flips']}")
 
 
+@pytest.mark.parametrize("T", [400, 700])
+def test_deepseek_block_grouping(T):
+    # more than 2048 routed pairs: grouped in blocks (per-block expert counts,
+    # then a stable scatter per block), with the shared experts' pairs after
+    # them; hot experts take the MFMA path (pairs of token tiles, odd counts)
+    c, L = cached_layer(4, (("E", 16), ("I", 256)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    assert T * L["K"] > 2048
+    tau = _tau(L, c, 0.85)
+    rows = np.unique(np.r_[0, 1, T // 3, T // 2, T - 2, T - 1])
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16, rows_idx=rows)
+    print(f"T={T} err={s['err']:.2e} band={s['band']} flips={s['flips']}")
+
+
 def test_deepseek_per_expert_tau():
     c, L = cached_layer(4)
     DL = layer_to_device(L)
