@@ -95,7 +95,8 @@ typedef struct {
  *           logit ranks as -infinity.
  *   out topk_w   [T,K] fp32: softmax probability of each chosen expert
  *           (computed over all E), divided by the sum of the K chosen ones
- *           when renormalize = 1.
+ *           when renormalize = 1.  A NaN or +infinity logit makes the
+ *           token's softmax denominator NaN, and so all its K weights.
  * Requires T >= 0, E >= 1, 1 <= K <= min(E, 32), E <= 512.
  */
 moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t K,
@@ -156,8 +157,12 @@ moe_status moe_workspace_size(const moe_shape *shape, int32_t mode, size_t *byte
  *   h_j = a_j * (x_t . w_up[e][j]) where m_j = 1, exactly 0 where m_j = 0
  *   o   = sum_j h_j * w_down[e][j]
  *   y_t = sum_{k<K} topk_w[t,k] * o_{t,k} + sum_{s<S} o_{t,K+s}
- * Rows of w_up and w_down that are inactive for every token routed to an
- * expert are not read.  A NaN score counts as active and propagates into y.
+ * Rows of w_down that are inactive for every token routed to an expert are
+ * not read; neither are such rows of w_up for an expert with fewer than 32
+ * routed pairs.  An expert with 32 or more (the bf16 matrix-core path)
+ * computes its up products for every row of each 64-row tile together with
+ * the gate, which reads each token tile's hidden states once; its h, and so
+ * y, are the same.  A NaN score counts as active and propagates into y.
  * Accumulation is fp32; the result is deterministic (no floating-point
  * atomics): the same inputs give bitwise-identical outputs.
  * Requires 16-byte aligned x and weights and a 256-byte aligned workspace.
