@@ -167,16 +167,16 @@ def test_qwen_prefill_sampled(q, mode):
 
 
 def test_mfma_and_gemv_paths_agree_at_threshold():
-    # a DeepSeek-style batch of 40 tokens: the 2 shared experts (40 pairs) and
-    # the hottest routed experts take the MFMA path, the rest the GEMV path;
-    # rows of both are checked against the oracle
+    # a DeepSeek-style batch of 40 tokens (H 2048: MFMA from 16 pairs): the 2
+    # shared experts (40 pairs) and the hottest routed experts take the MFMA
+    # path, the rest the GEMV path; rows of both are checked against the oracle
     c, L = cached_layer(4)
     DL = layer_to_device(L)
     x, logits = synth.make_tokens(c, 2, 40)
     tau = _tau(L, c, 0.85, calib_tokens=16)
     ids = np.argsort(-logits, axis=1, kind="stable")[:, :L["K"]]
     counts = np.bincount(ids.ravel(), minlength=L["E"])
-    assert counts.max() >= 32 > counts.min()
+    assert counts.max() >= 16 > counts.min()
     check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
 
 
