@@ -19,7 +19,9 @@
 // partial sum per piece (at most KMAX); the combine kernel adds the pieces
 // and the K slots in a fixed order, so no floating-point atomics are used and
 // the result is bitwise reproducible.  Every workgroup derives the same
-// schedule from the per-slot union sizes; workgroup 0 also stores it for the
+// schedule from the per-slot union sizes.  Outputs are indexed by (token,
+// slot): piece k of pair (t, slot) is row t * slots + slot of partial slice
+// k, and the last piece of a group stores the group's piece count for the
 // combine.
 #include <type_traits>
 

@@ -23,7 +23,8 @@
 //         neuron contributes exactly 0).
 // h goes to a per-expert block [rows][n_e]; rows inactive for every token of
 // the tile get h = 0 without reading w_up.  Mask words and the per-expert
-// union word are written whole, without atomics in global memory.
+// union word are written whole, without atomics; only the union sizes are
+// summed, by integer atomics (order-independent).
 #include <type_traits>
 
 #include "mfma_body.h"
