@@ -27,6 +27,7 @@
 
 #include "mfma_body.h"
 #include "moe_internal.h"
+#include "wave_reduce.h"
 
 namespace moe {
 
@@ -84,20 +85,6 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 // popcounts finds the word holding position a, so the visit starts there
 // (not at word 0) and stops once position b is reached.
 constexpr int kMaxWordsPerLane = kMaxRows / 32 / kWave;  // 8
-
-// Inclusive prefix sum over the 64 lanes: DPP row shifts within each row of
-// 16 lanes (out-of-row sources read 0), then row broadcasts of lanes 15 and
-// 31 into the rows after them.
-__device__ __forceinline__ int wave_incl_scan_dpp(int x)
-{
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
-    return x;
-}
 
 // The ballot walk over word pairs [2 kk0, ...) of one register of words,
 // starting at union position base; returns the position after the walk.

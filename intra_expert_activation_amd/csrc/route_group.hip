@@ -160,10 +160,18 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     const int a_end = min(re, rb + (wv + 1) * per_wave * kWave);
 
     // pass 1: per-wavefront counts (the ids of kIdBatch chunks are loaded at
-    // once: one memory latency per batch instead of one per chunk)
+    // once: one memory latency per batch instead of one per chunk; the first
+    // batch stays in registers for pass 2)
+    int ev0[kIdBatch];
+    if (a_begin < a_end) load_id_batch(ids, a_begin, a_end, lane, ev0);
     for (int b0 = a_begin; b0 < a_end; b0 += kIdBatch * kWave) {
         int ev[kIdBatch];
-        load_id_batch(ids, b0, a_end, lane, ev);
+        if (b0 == a_begin) {
+#pragma unroll
+            for (int j = 0; j < kIdBatch; ++j) ev[j] = ev0[j];
+        } else {
+            load_id_batch(ids, b0, a_end, lane, ev);
+        }
 #pragma unroll
         for (int j = 0; j < kIdBatch; ++j) {
             const int base = b0 + j * kWave;
@@ -212,12 +220,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             loc[i] = e < EX ? s_off[e] : 0;
             sum += loc[i];
         }
-        int incl = sum;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int o = __shfl_up(incl, s, kWave);
-            if (lane >= s) incl += o;
-        }
+        const int incl = wave_incl_scan_dpp(sum);
         int run = incl - sum;
         int ntouched_before = 0;
         // touched list needs the counts in ascending expert order
@@ -241,12 +244,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         }
       if (writer) {
         // touched experts, ascending: exclusive prefix of per-lane touched counts
-        int tincl = ntouched_before;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int o = __shfl_up(tincl, s, kWave);
-            if (lane >= s) tincl += o;
-        }
+        const int tincl = wave_incl_scan_dpp(ntouched_before);
         int tpos = tincl - ntouched_before;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -271,12 +269,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             const int e = lane * kPer + i;
             if (e < EX && loc[i] >= p.nm) tiles += (loc[i] + kMfmaTokens - 1) / kMfmaTokens;
         }
-        int iincl = tiles;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int o = __shfl_up(iincl, s, kWave);
-            if (lane >= s) iincl += o;
-        }
+        const int iincl = wave_incl_scan_dpp(tiles);
         // and the projection's item pairs (two adjacent token tiles of one
         // expert, or its last tile alone): (first item index << 1) | has second
         int npairs = 0;
@@ -285,12 +278,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             const int e = lane * kPer + i;
             if (e < EX && loc[i] >= p.nm) npairs += ((loc[i] + kMfmaTokens - 1) / kMfmaTokens + 1) / 2;
         }
-        int pincl = npairs;
-#pragma unroll
-        for (int s = 1; s < kWave; s <<= 1) {
-            const int o = __shfl_up(pincl, s, kWave);
-            if (lane >= s) pincl += o;
-        }
+        const int pincl = wave_incl_scan_dpp(npairs);
         int ipos = iincl - tiles, ppos = pincl - npairs;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -320,7 +308,12 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     // pass 2: stable scatter of the routed pairs
     for (int b0 = a_begin; b0 < a_end; b0 += kIdBatch * kWave) {
         int ev[kIdBatch];
-        load_id_batch(ids, b0, a_end, lane, ev);
+        if (b0 == a_begin) {
+#pragma unroll
+            for (int j = 0; j < kIdBatch; ++j) ev[j] = ev0[j];
+        } else {
+            load_id_batch(ids, b0, a_end, lane, ev);
+        }
 #pragma unroll
         for (int j = 0; j < kIdBatch; ++j) {
             const int base = b0 + j * kWave;

@@ -172,4 +172,18 @@ __device__ __forceinline__ float wave_sum_all(float v)
     }));
 }
 
+// Inclusive prefix sum over the 64 lanes: DPP row shifts within each row of
+// 16 lanes (out-of-row sources read 0), then row broadcasts of lanes 15 and
+// 31 into the rows after them.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 }  // namespace moe
