@@ -159,8 +159,7 @@ moe_status moe_workspace_size(const moe_shape *shape, int32_t mode, size_t *byte
  *   y_t = sum_{k<K} topk_w[t,k] * o_{t,k} + sum_{s<S} o_{t,K+s}
  * Rows of w_down that are inactive for every token routed to an expert are
  * not read; neither are such rows of w_up for an expert with fewer than 16
- * routed pairs (32 when H > 2048).  An expert with more (the bf16
- * matrix-core path)
+ * routed pairs.  An expert with more (the bf16 matrix-core path)
  * computes its up products for every row of each 64-row tile together with
  * the gate, which reads each token tile's hidden states once; its h, and so
  * y, are the same.  A NaN score counts as active and propagates into y.

@@ -93,20 +93,18 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // x 14336 rows: 128 workgroups, 1.1 TB/s)
     p->GD = 1024;
 
-    // MFMA path: bf16 experts with at least nm pairs.  A routed expert has at
-    // most T pairs, so with T below the threshold it is off.  nm is 16 when
-    // the GEMV body holds one 16-byte vector per lane per row (H <= 2048):
-    // an expert with 16 to 31 pairs then costs the GEMV body 2 to 4 passes
-    // over its rows, more than a mostly idle 128-token MFMA tile (DeepSeek-
-    // style layer, T 64: 211 -> 193 us).  With wider rows the merged launch's
-    // GEMV body needs more registers than 3 workgroups per CU allow, and 32
-    // keeps small batches off it.
+    // MFMA path: bf16 experts with at least nm = 16 pairs.  A routed expert has
+    // at most T pairs, so with T below the threshold it is off.  An expert with
+    // 16 to 31 pairs costs the GEMV body 2 to 4 passes over its rows (from HBM
+    // once its rows outgrow L2), more than a mostly idle 128-token MFMA tile:
+    // DeepSeek-style layer, T 64: 211 -> 193 us; Mixtral-style, T 128: the
+    // measurement is in the design notes.
     p->nm = INT_MAX;
     p->use_mfma = 0;
     p->NT = (p->Imax + 63) / 64;
     p->max_items = 0;
     p->max_pairs = 0;
-    const int nm = p->NS <= 4 ? kMfmaMinPairsNarrow : kMfmaMinPairs;
+    const int nm = kMfmaMinPairs;
     if (!calib && p->dtype == MOE_BF16 && T >= nm) {
         p->nm = nm;
         p->use_mfma = 1;

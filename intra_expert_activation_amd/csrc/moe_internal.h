@@ -17,8 +17,7 @@ constexpr int kMaxRows = 16384;    // I, I_shared
 constexpr int kMaxRowsPerChunk = 256;
 constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
 constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
-constexpr int kMfmaMinPairs = 32;  // pair-count threshold of the MFMA path
-constexpr int kMfmaMinPairsNarrow = 16;  // the same for H <= 2048 (bf16)
+constexpr int kMfmaMinPairs = 16;  // pair-count threshold of the MFMA path
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a

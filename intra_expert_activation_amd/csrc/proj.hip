@@ -329,7 +329,10 @@ template <class Tr, int NW, int NSW, int TT, int MODE>
 static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, hipStream_t st)
 {
     const bool mfma = MODE != kModeScore && pl.use_mfma;
-    if constexpr (std::is_same<Tr, BF16>::value && NW == 4) {
+    // one 16-byte vector per lane per row only: with more, the merged kernel's
+    // GEMV body does not fit 3 workgroups per CU, and the MFMA tiles get a
+    // launch of their own
+    if constexpr (std::is_same<Tr, BF16>::value && NW == 4 && NSW == 1) {
         if (mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
             const int mfma_blocks = round8((long long)pl.max_pairs * pl.NT);
             const int grid = mfma_blocks + pl.max_touched * pl.C;

@@ -167,7 +167,7 @@ def test_qwen_prefill_sampled(q, mode):
 
 
 def test_mfma_and_gemv_paths_agree_at_threshold():
-    # a DeepSeek-style batch of 40 tokens (H 2048: MFMA from 16 pairs): the 2
+    # a DeepSeek-style batch of 40 tokens (MFMA from 16 pairs): the 2
     # shared experts (40 pairs) and the hottest routed experts take the MFMA
     # path, the rest the GEMV path; rows of both are checked against the oracle
     c, L = cached_layer(4)
