@@ -12,7 +12,7 @@ import torch
 import oracle
 from intra_expert_activation_amd import moe, synth
 
-from parity_util import cached_layer, check_layer, gpu_ffn, layer_to_device, rel_l2, unpack_bits
+from parity_util import cached_layer, check_layer, dev_tensor, gpu_ffn, layer_to_device, rel_l2, unpack_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -247,6 +247,54 @@ def test_deterministic():
     b = gpu_ffn(DL, x, logits, tau)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64)])
+def test_graph_replay_matches_eager(cfg, T):
+    # the benchmark's launch configuration: calls captured in one HIP graph
+    # (one per batch, in order, sharing a workspace) and replayed several times
+    # with eager work between the replays; every replay must reproduce the
+    # eager calls bit for bit
+    c, L = cached_layer(cfg)
+    DL = layer_to_device(L)
+    tau = torch.from_numpy(np.broadcast_to(np.asarray(_tau(L, c, 0.85, calib_tokens=16), np.float32),
+                                           (L["E"] + L["S"],)).copy()).cuda()
+    shared = (DL["ws_gate"], DL["ws_up"], DL["ws_down"]) if L["S"] else None
+    batches = []
+    for r in range(3):
+        x, lg = synth.make_tokens(c, 2, (r + 1) * T)
+        batches.append((dev_tensor(x[r * T:], DL["dtype"]), torch.from_numpy(np.ascontiguousarray(lg[r * T:])).cuda()))
+    shape = moe.layer_shape(batches[0][0], DL["w_gate"], L["K"], bool(L["renormalize"]), shared[0] if shared else None)
+    ws = moe.alloc_workspace(moe.workspace_size(shape), "cuda")
+
+    def call(r, out=None):
+        x, lg = batches[r]
+        return moe.sparse_expert_ffn(x, lg, DL["w_gate"], DL["w_up"], DL["w_down"], tau, K=L["K"],
+                                     renormalize=bool(L["renormalize"]), shared=shared, out=out, workspace=ws)
+
+    eager = [{k: v.clone() for k, v in call(r).items()} for r in range(3)]
+    outs = [{k: torch.empty_like(v) for k, v in e.items()} for e in eager]
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            for r in range(3):
+                call(r, outs[r])
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            for v in o.values():
+                v.fill_(-1)
+        call(rep % 3)  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(3):
+            for k in ("y", "mask_bits", "topk_ids", "topk_w", "union_cnt"):
+                assert torch.equal(outs[r][k], eager[r][k]), (rep, r, k)
 
 
 # ---------------------------------------------------------------------------
