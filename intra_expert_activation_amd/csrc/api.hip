@@ -142,6 +142,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_items = take((size_t)p->max_items * 4);
     p->off_pairs = take((size_t)p->max_pairs * 4);
     p->off_blockcnt = take((size_t)((p->A + kGroupBlock - 1) / kGroupBlock) * p->E * 4);
+    p->off_order = take((size_t)p->EX * 4);
     p->off_nact = take(blocks * 4);
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);
@@ -261,12 +262,13 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     gp.items = ws_at<int32_t>(ws, pl.off_items);
     gp.pairs = ws_at<int32_t>(ws, pl.off_pairs);
     gp.blockcnt = ws_at<int32_t>(ws, pl.off_blockcnt);
+    gp.order = ws_at<int32_t>(ws, pl.off_order);
     if (launch_route_group(a->router_logits, pl.renorm, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
     pp.x = a->x; pp.wg = a->w_gate; pp.wu = a->w_up; pp.swg = a->ws_gate; pp.swu = a->ws_up;
     pp.tau = a->tau;
-    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched;
+    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched; pp.order = gp.order;
     pp.pair_tok = pair_tok; pp.pair_slot = pair_slot;
     pp.h = h; pp.mask_bits = a->mask_bits; pp.union_words = union_words; pp.ucount = ucount;
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;
@@ -353,12 +355,13 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr; gp.pairs = nullptr;
     gp.blockcnt = ws_at<int32_t>(workspace, pl.off_blockcnt);
+    gp.order = ws_at<int32_t>(workspace, pl.off_order);
     if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
 
     ProjParams pp{};
     pp.x = x_calib; pp.wg = w_gate; pp.wu = w_gate; pp.swg = ws_gate; pp.swu = ws_gate;
     pp.tau = nullptr;
-    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched;
+    pp.hdr = hdr; pp.counts = counts; pp.offsets = offsets; pp.touched = touched; pp.order = gp.order;
     pp.pair_tok = pair_tok; pp.pair_slot = pair_slot;
     pp.h = scores; pp.mask_bits = nullptr; pp.union_words = nullptr;
     pp.H = pl.H; pp.E = pl.E; pp.I = pl.I; pp.Is = pl.Is; pp.S = pl.S; pp.K = pl.K; pp.A = pl.A;

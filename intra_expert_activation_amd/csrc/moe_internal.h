@@ -53,7 +53,7 @@ struct Plan {
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
     size_t off_taus;
-    size_t off_items, off_pairs, off_blockcnt, off_nact, off_list, off_hhi, off_hlo;
+    size_t off_items, off_pairs, off_blockcnt, off_order, off_nact, off_list, off_hhi, off_hlo;
     size_t total;
 };
 
@@ -83,6 +83,7 @@ struct GroupParams {
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
     int32_t *pairs;       // [max_pairs] (first item << 1 | has a second) for the MFMA projection
     int32_t *blockcnt;    // [ceil(A / kGroupBlock), E] per-block expert counts (large batches), or null
+    int32_t *order;       // [EX] (slot << 16 | expert) of the touched experts, by descending pair count
 };
 
 struct ProjParams {
@@ -90,6 +91,7 @@ struct ProjParams {
     const void *wg, *wu, *swg, *swu;
     const float *tau;
     const int32_t *hdr, *counts, *offsets, *touched, *pair_tok, *pair_slot;
+    const int32_t *order; // GroupParams::order: the order in which workgroups take the experts
     float *h;             // per-expert blocks [rows][n_e] (fp32)
     uint32_t *mask_bits;  // optional output [T,slots,W]
     uint32_t *union_words;// [EX,W]

@@ -244,10 +244,12 @@ template <class Tr, int NW, int NSW, int TTMAX, int MODE>
 __device__ __forceinline__ void proj_gemv(const ProjParams &p, ProjLds<NW, TTMAX> &L, int bid)
 {
     using V = typename Tr::V;
-    const int s = bid / p.C;
-    const int c = bid - s * p.C;
-    if (s >= p.hdr[0]) return;
-    const int xe = p.touched[s];
+    const int r = bid / p.C;  // rank of the expert in the longest-first order
+    const int c = bid - r * p.C;
+    if (r >= p.hdr[0]) return;
+    const int ord = p.order[r];
+    const int s = ord >> 16;  // touched slot
+    const int xe = ord & 0xffff;
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
     const int r0 = c * kChunk;

@@ -146,6 +146,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     __shared__ int s_cnt[kGroupWaves][kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_before[kMaxExperts];  // this expert's pairs in earlier blocks
+    __shared__ int s_tot[kMaxExperts];     // pairs per expert (the whole batch)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -206,6 +207,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             run = p.T;  // a shared expert serves every token
         }
         s_off[e] = run;  // total for now
+        s_tot[e] = run;
         s_before[e] = before;
     }
     __syncthreads();
@@ -296,6 +298,65 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             p.hdr[2] = pincl;
         }
       }
+    } else if (wv == 1 && writer && p.order) {
+        // The order in which the GEMV projection takes the touched experts:
+        // by descending pair count (16 or more share the first class), ties
+        // by slot.  Longest first keeps the experts that need two token tiles
+        // (more than 8 pairs) from starting last and trailing the grid.  A
+        // stable counting sort over 16 classes, in this wavefront while
+        // wavefront 0 writes the metadata: a lane's class counts are packed
+        // three to an int, 10 bits each (a class holds at most 512 experts,
+        // so no field carries into the next), and summed across the lanes by
+        // prefix scans.
+        constexpr int kPer = kMaxExperts / kWave;
+        constexpr int kCls = 16;
+        constexpr int kWords = (kCls + 2) / 3;
+        int cls[kPer];
+        int cnt[kWords];
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) cnt[j] = 0;
+        int ntl = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            const int n = e < EX ? s_tot[e] : 0;
+            cls[i] = n <= 0 ? -1 : (n >= kCls ? 0 : kCls - n);
+            if (n > 0) {
+                ++ntl;
+#pragma unroll
+                for (int j = 0; j < kWords; ++j) cnt[j] += (cls[i] / 3 == j) ? 1 << (10 * (cls[i] % 3)) : 0;
+            }
+        }
+        int slot = wave_incl_scan_dpp(ntl) - ntl;  // slot of this lane's first touched expert
+        int pos[kWords];  // next position of each class for this lane, packed
+        int run = 0;      // experts in the classes before (uniform)
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) {
+            const int incl = wave_incl_scan_dpp(cnt[j]);
+            const int tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+            int base = 0;
+#pragma unroll
+            for (int f = 0; f < 3; ++f)
+                if (3 * j + f < kCls) {
+                    base |= run << (10 * f);
+                    run += (tot >> (10 * f)) & 1023;
+                }
+            pos[j] = base + incl - cnt[j];
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int c = cls[i];
+            if (c >= 0) {
+                const int sh = 10 * (c % 3);
+                int w = 0;
+#pragma unroll
+                for (int j = 0; j < kWords; ++j) w = (c / 3 == j) ? pos[j] : w;
+                p.order[(w >> sh) & 1023] = (slot << 16) | (lane * kPer + i);
+#pragma unroll
+                for (int j = 0; j < kWords; ++j) pos[j] += (c / 3 == j) ? 1 << sh : 0;
+                ++slot;
+            }
+        }
     }
     __syncthreads();
     // union words of the MFMA experts are built with atomic ORs: clear them
