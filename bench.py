@@ -40,7 +40,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_projection_qwen_de
 # sources compiled into the expert projection kernel: a stored HBM-traffic
 # measurement is used only while they are unchanged
 KERNEL_SRCS = [os.path.join(ROOT, "intra_expert_activation_amd", "csrc", f)
-               for f in ("proj.hip", "mfma_body.h", "moe_internal.h", "wave_reduce.h")]
+               for f in ("proj.hip", "gemv_rows.h", "mfma_body.h", "moe_internal.h", "wave_reduce.h")]
 
 
 def kernel_src_sha256():

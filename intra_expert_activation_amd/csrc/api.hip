@@ -115,6 +115,9 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
         p->max_pairs = (p->max_items + big + p->S + 1) / 2;
     }
 
+    // one-launch decode path: single-token batches (every expert has one pair)
+    p->fused = (!calib && T >= 1 && T <= kFusedMaxT) ? 1 : 0;
+
     // workspace layout
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -136,7 +139,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_ucount = take((size_t)p->EX * 4);
     p->off_npc = take(calib ? 0 : (size_t)p->P * p->NCT * 4);
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
-    p->off_partial = take(calib ? 0 : (size_t)p->KMAX * p->P * p->H * 4);
+    p->off_partial = take(calib ? 0 : (size_t)(p->fused ? p->C : p->KMAX) * p->P * p->H * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
     const size_t blocks = (size_t)p->max_items * p->NT;
     p->off_items = take((size_t)p->max_items * 4);
@@ -147,6 +150,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);
     p->off_hlo = take(blocks * 64 * 64 * 2);
+    p->off_mw = take(p->fused ? (size_t)p->P * p->W * 4 : 0);
     p->total = o;
     return MOE_OK;
 }
@@ -248,6 +252,23 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     int32_t *npc = ws_at<int32_t>(ws, pl.off_npc);
     float *h = ws_at<float>(ws, pl.off_h);
     float *partial = ws_at<float>(ws, pl.off_partial);
+
+    if (pl.fused) {
+        FusedParams fp{};
+        fp.logits = a->router_logits;
+        fp.x = a->x; fp.wg = a->w_gate; fp.wu = a->w_up; fp.wd = a->w_down;
+        fp.swg = a->ws_gate; fp.swu = a->ws_up; fp.swd = a->ws_down;
+        fp.tau = a->tau;
+        fp.ids = ids; fp.w = w; fp.partial = partial; fp.mw = ws_at<uint32_t>(ws, pl.off_mw);
+        fp.mask_bits = a->mask_bits; fp.union_idx = a->union_idx; fp.union_cnt = a->union_cnt;
+        fp.y = a->y;
+        fp.T = pl.T; fp.H = pl.H; fp.E = pl.E; fp.I = pl.I; fp.Is = pl.Is; fp.S = pl.S; fp.K = pl.K;
+        fp.slots = pl.slots; fp.P = pl.P; fp.C = pl.C; fp.W = pl.W; fp.Imax = pl.Imax; fp.renorm = pl.renorm;
+        return launch_fused(pl, fp, mode, (hipEvent_t)a->prof_event_begin, (hipEvent_t)a->prof_event_end, stream)
+                       == hipSuccess
+                   ? MOE_OK
+                   : MOE_ERR_HIP;
+    }
 
     GroupParams gp{};
     gp.ids = ids;

@@ -18,6 +18,7 @@ constexpr int kMaxRowsPerChunk = 256;
 constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
 constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
 constexpr int kMfmaMinPairs = 16;  // pair-count threshold of the MFMA path
+constexpr int kFusedMaxT = 1;      // batches of at most this many tokens take the one-launch decode path
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a
@@ -49,11 +50,15 @@ struct Plan {
     int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
     int max_items;   // upper bound on (expert, 64-token tile) work items
     int max_pairs;   // upper bound on pairs of them (the MFMA projection's items)
+    // one-launch decode path (T <= kFusedMaxT): every (pair, 32-row chunk)
+    // runs routing, gate, mask, up and down; a second launch combines
+    int fused;
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
     size_t off_taus;
     size_t off_items, off_pairs, off_blockcnt, off_order, off_nact, off_list, off_hhi, off_hlo;
+    size_t off_mw;
     size_t total;
 };
 
@@ -142,6 +147,22 @@ struct MfmaParams {
     int H, E, I, Is, S, W, Imax, slots, NT, max_items, max_pairs, NCT;
 };
 
+// One-launch decode path.  Pair p = t * slots + slot; chunk c = rows
+// [32c, 32c + 32) of the pair's expert.
+struct FusedParams {
+    const float *logits;  // [T,E]
+    const void *x, *wg, *wu, *wd, *swg, *swu, *swd;
+    const float *tau;
+    int32_t *ids;         // [T,K] routing outputs (the caller's or the workspace's)
+    float *w;             // [T,K]
+    float *partial;       // [P, C, H]: chunk c's down partial sum of pair p
+    uint32_t *mw;         // [P, W] mask words (always written)
+    uint32_t *mask_bits;  // optional output [P, W]
+    int32_t *union_idx, *union_cnt;  // optional outputs
+    float *y;
+    int T, H, E, I, Is, S, K, slots, P, C, W, Imax, renorm;
+};
+
 struct SelectParams {
     const float *scores;  // |SiLU| per (pair, neuron), expert blocks as ProjParams::h
     const int32_t *counts, *offsets;
@@ -168,6 +189,10 @@ hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t s
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
 hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_down_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
+// The one-launch decode path and its combine; the events (optional) bracket
+// the first launch.
+hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEvent_t ev_begin, hipEvent_t ev_end,
+                        hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -5,6 +5,7 @@
 // 2605.08575, Technical Summary, Methodology: router logic preserved); the
 // grouping is what lets every expert process its tokens as one batch.
 #include "moe_internal.h"
+#include "route.h"
 #include "wave_reduce.h"
 
 namespace moe {
@@ -14,78 +15,19 @@ namespace moe {
 // K rounds of a wavefront arg-max pick the experts in descending logit order
 // (ties to the lower id); softmax weights are exp(l - max) / sum exp(l - max).
 // ---------------------------------------------------------------------------
-// Weight of a chosen expert with exp value ev: its softmax probability
-// ev / denom, or renormalised over the K chosen, ev / sel_sum (the same
-// quotient of probabilities with denom cancelled).  A NaN denominator (a NaN
-// or +inf logit) makes every probability NaN, and so every weight.
-__device__ __forceinline__ float slot_weight(float ev, float sel_sum, float denom, int renorm)
-{
-    if (!renorm) return ev / denom;
-    return isnan(denom) ? denom : ev / sel_sum;
-}
-
-// Routes token t with one wavefront.
-__device__ __forceinline__ void route_token(const float *__restrict__ logits, int t, int E, int K, int renorm,
-                                            int32_t *__restrict__ ids, float *__restrict__ w)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const float *l = logits + (size_t)t * E;
-    constexpr int kPer = kMaxExperts / kWave;
-    float v[kPer];      // ranking value (NaN ranks as -inf)
-    float raw[kPer];    // logit as given
-    uint32_t avail = 0; // bit i: expert lane + 64 i is present and not yet chosen
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + kWave * i;
-        raw[i] = e < E ? l[e] : 0.f;
-        v[i] = (e < E && !isnan(raw[i])) ? raw[i] : -INFINITY;
-        if (e < E) avail |= 1u << i;
-    }
-    // maximum over the non-NaN logits, for a range-safe softmax
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if ((avail >> i) & 1u) m = fmaxf(m, v[i]);
-    m = wave_max(m);
-    float denom = 0.f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if ((avail >> i) & 1u) denom += expf(raw[i] - m);
-    denom = wave_sum_all(denom);
-
-    float chosen_e = 0.f;  // lane k keeps exp(l - m) of slot k
-    float sel_sum = 0.f;
-    for (int k = 0; k < K; ++k) {
-        // lane-local best available expert (ascending ids: ties keep the lower)
-        float bv = -INFINITY, braw = 0.f;
-        int bid = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            if (((avail >> i) & 1u) && (bid == 0x7fffffff || v[i] > bv)) {
-                bv = v[i];
-                braw = raw[i];
-                bid = lane + kWave * i;
-            }
-        }
-        // wavefront arg-max: the largest value, then the lowest id holding it
-        const float top = wave_max(bid == 0x7fffffff ? -INFINITY : bv);
-        const int win = wave_min((bid != 0x7fffffff && bv == top) ? bid : 0x7fffffff);
-        const float wraw = __shfl(braw, win & (kWave - 1), kWave);  // the chosen logit, as given
-        if ((win & (kWave - 1)) == lane) avail &= ~(1u << (win / kWave));
-        const float ev = expf(wraw - m);
-        if (lane == k) chosen_e = ev;
-        sel_sum += ev;
-        if (lane == 0) ids[(size_t)t * K + k] = win;
-    }
-    if (lane < K) w[(size_t)t * K + lane] = slot_weight(chosen_e, sel_sum, denom, renorm);
-}
-
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E, int K,
                                                int renorm, int32_t *__restrict__ ids, float *__restrict__ w)
 {
     const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
     if (t >= T) return;
-    route_token(logits, t, E, K, renorm, ids, w);
+    int id;
+    float wt;
+    route_token(logits, t, E, K, renorm, id, wt);
+    const int lane = threadIdx.x & (kWave - 1);
+    if (lane < K) {
+        ids[(size_t)t * K + lane] = id;
+        w[(size_t)t * K + lane] = wt;
+    }
 }
 
 hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,

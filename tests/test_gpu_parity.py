@@ -249,7 +249,7 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64)])
+@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64), (2, 1), (4, 1)])
 def test_graph_replay_matches_eager(cfg, T):
     # the benchmark's launch configuration: calls captured in one HIP graph
     # (one per batch, in order, sharing a workspace) and replayed several times
@@ -295,6 +295,59 @@ def test_graph_replay_matches_eager(cfg, T):
         for r in range(3):
             for k in ("y", "mask_bits", "topk_ids", "topk_w", "union_cnt"):
                 assert torch.equal(outs[r][k], eager[r][k]), (rep, r, k)
+
+
+# ---------------------------------------------------------------------------
+# Single-token batches: the one-launch path (routing, gate, mask, up and down
+# in one workgroup per (slot, 32-row chunk), then the combine launch)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,over,q", [
+    (1, (), 0.8),                                                   # fp32, H 256 (one wavefront)
+    (1, (("H", 512), ("I", 160), ("E", 5)), 0.6),                   # fp32, two wavefronts
+    (2, (), 0.85),                                                  # Qwen-style
+    (2, (("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 0.85),         # 16 vectors per lane
+    (2, (("H", 512), ("E", 2), ("I", 16384), ("K", 1)), 0.85),       # 512 chunks per slot
+    (2, (("E", 4), ("K", 4)), 0.85),                                # K = E
+    (3, (("I", 1024),), 0.9),                                       # Mixtral-style H 4096
+    (4, (), 0.85),                                                  # DeepSeek-style, shared experts
+    (4, (("E", 12), ("I", 128), ("I_shared", 320), ("S", 1)), 0.7),  # shared wider than routed
+])
+def test_single_token_path(cfg, over, q):
+    c, L = cached_layer(cfg, over)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 6)
+    tau = _tau(L, c, q, calib_tokens=8)
+    tol = TOL_F32 if L["dtype"] == "f32" else TOL_BF16
+    for t in range(x.shape[0]):  # six tokens, one call each
+        check_layer(L, DL, x[t:t + 1], logits[t:t + 1], tau, tol=tol)
+    check_layer(L, DL, x[:1], logits[:1], None, mode=moe.MOE_DENSE, tol=tol)
+
+
+def test_single_token_edge_cases():
+    c, L = cached_layer(4, (("E", 16), ("I", 256)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 4)
+    x1, l1 = x[2:3], logits[2:3]
+    # tau = 0 keeps every neuron: bitwise the dense layer
+    sp, de = gpu_ffn(DL, x1, l1, 0.0), gpu_ffn(DL, x1, l1, None, mode=moe.MOE_DENSE)
+    assert np.array_equal(sp["y"], de["y"]) and np.array_equal(sp["mask_bits"], de["mask_bits"])
+    # tau = inf keeps none
+    g = gpu_ffn(DL, x1, l1, np.inf)
+    assert (g["y"] == 0).all() and (g["mask_bits"] == 0).all() and (g["union_cnt"] == 0).all()
+    # a NaN hidden state is active and propagates
+    tau = _tau(L, c, 0.8, calib_tokens=8)
+    xn = x1.copy()
+    xn[0, 5] = 0x7FC0  # a bf16 NaN (the layer's hidden states are bf16 bit patterns)
+    g = gpu_ffn(DL, xn, l1, tau)
+    assert np.isnan(g["y"]).all() and unpack_bits(g["mask_bits"], L["I"]).all()
+    # without the optional outputs (routing kept in the workspace, no unions)
+    full = gpu_ffn(DL, x1, l1, tau)
+    bare = gpu_ffn(DL, x1, l1, tau, want_masks=False)
+    assert np.array_equal(full["y"], bare["y"])
+    # repeated calls are bitwise identical
+    again = gpu_ffn(DL, x1, l1, tau)
+    for k in full:
+        assert np.array_equal(full[k], again[k]), k
 
 
 # ---------------------------------------------------------------------------
