@@ -1,4 +1,5 @@
-// One-launch decode path for batches of at most kFusedMaxT tokens.
+// One-launch decode path for small batches (single tokens, and up to
+// kFusedMaxT tokens of layers with small experts).
 //
 // gist.science page of arXiv 2605.08575, Technical Summary, Methodology:
 // the gate projection is dense, the threshold mask is one elementwise pass,
@@ -16,8 +17,10 @@
 //
 // With one token per batch every expert serves exactly one pair, so the
 // grouping and the separate down launch (its schedule and row lists are a
-// chain of dependent memory round trips) cost more than they organise.  The
-// partial rows add 4 * H bytes per 32 neuron rows: 1/16 of the gate bytes,
+// chain of dependent memory round trips) cost more than they organise.  With a
+// few tokens an expert chosen by several of them has its rows read once per
+// pair, mostly from cache while those workgroups run together.  The partial
+// rows add 4 * H bytes per 32 neuron rows and pair: 1/16 of the gate bytes,
 // written and read once.
 #include "gemv_rows.h"
 #include "moe_internal.h"

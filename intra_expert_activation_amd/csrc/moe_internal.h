@@ -18,7 +18,7 @@ constexpr int kMaxRowsPerChunk = 256;
 constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
 constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
 constexpr int kMfmaMinPairs = 16;  // pair-count threshold of the MFMA path
-constexpr int kFusedMaxT = 1;      // batches of at most this many tokens take the one-launch decode path
+constexpr int kFusedMaxT = 8;      // most tokens of a batch on the one-launch decode path
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a
@@ -50,7 +50,7 @@ struct Plan {
     int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
     int max_items;   // upper bound on (expert, 64-token tile) work items
     int max_pairs;   // upper bound on pairs of them (the MFMA projection's items)
-    // one-launch decode path (T <= kFusedMaxT): every (pair, 32-row chunk)
+    // one-launch decode path (small batches): every (pair, 32-row chunk)
     // runs routing, gate, mask, up and down; a second launch combines
     int fused;
     // workspace layout (byte offsets)

@@ -183,12 +183,14 @@ def test_mfma_and_gemv_paths_agree_at_threshold():
 # ---------------------------------------------------------------------------
 # Edge cases
 # ---------------------------------------------------------------------------
+# batches of more than 8 tokens: the grouped path (smaller ones are covered
+# by the one-launch tests below)
 @pytest.mark.parametrize("over,T", [
-    ((("E", 4), ("K", 4)), 5),                                      # K = E
+    ((("E", 4), ("K", 4)), 11),                                     # K = E
     ((("E", 300), ("K", 3), ("I", 64)), 50),                        # many experts
-    ((("H", 512), ("E", 6), ("I", 96), ("K", 2)), 7),               # H = 512 (one vector per lane)
-    ((("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 3),              # H = 8192 (16 vectors per lane)
-    ((("H", 512), ("E", 2), ("I", 16384), ("K", 1)), 5),            # I = 16384 (the largest), KMAX pieces
+    ((("H", 512), ("E", 6), ("I", 96), ("K", 2)), 13),              # H = 512 (one vector per lane)
+    ((("H", 8192), ("E", 4), ("I", 64), ("K", 2)), 9),              # H = 8192 (16 vectors per lane)
+    ((("H", 512), ("E", 2), ("I", 16384), ("K", 1)), 10),           # I = 16384 (the largest), KMAX pieces
 ])
 def test_edge_shapes_bf16(over, T):
     c, L = cached_layer(2, over)
@@ -249,7 +251,7 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64), (2, 1), (4, 1)])
+@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64), (2, 1), (4, 1), (4, 8)])
 def test_graph_replay_matches_eager(cfg, T):
     # the benchmark's launch configuration: calls captured in one HIP graph
     # (one per batch, in order, sharing a workspace) and replayed several times
@@ -321,6 +323,22 @@ def test_single_token_path(cfg, over, q):
     for t in range(x.shape[0]):  # six tokens, one call each
         check_layer(L, DL, x[t:t + 1], logits[t:t + 1], tau, tol=tol)
     check_layer(L, DL, x[:1], logits[:1], None, mode=moe.MOE_DENSE, tol=tol)
+
+
+@pytest.mark.parametrize("cfg,T,q", [(2, 2, 0.85), (2, 4, 0.85), (2, 8, 0.70), (4, 3, 0.85), (4, 8, 0.85),
+                                     (1, 5, 0.8), (3, 2, 0.9)])
+def test_few_token_batches(cfg, T, q):
+    # up to 8 tokens of small-expert layers take the one-launch path (an
+    # expert chosen by several tokens, and the shared experts, have several
+    # pairs whose masks form its union); the Mixtral-style layer's 2 tokens
+    # take the grouped path
+    c, L = cached_layer(cfg, (("I", 4096),) if cfg == 3 else ())  # 32 MiB of gate per expert
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 3 * T)
+    tau = _tau(L, c, q, calib_tokens=8)
+    tol = TOL_F32 if L["dtype"] == "f32" else TOL_BF16
+    for r in range(3):
+        check_layer(L, DL, x[r * T:(r + 1) * T], logits[r * T:(r + 1) * T], tau, tol=tol)
 
 
 def test_single_token_edge_cases():
