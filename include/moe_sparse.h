@@ -136,7 +136,11 @@ typedef struct {
     size_t workspace_bytes;     /* >= moe_workspace_size(shape, mode) */
     void *prof_event_begin;     /* optional hipEvent_t recorded on the stream
                                    just before the expert projection kernel
-                                   (gate/score/mask/up); NULL for none */
+                                   (gate/score/mask/up; for batches of one
+                                   token, and of up to 8 tokens when an
+                                   expert's gate holds at most 16 MiB, the
+                                   kernel that also runs routing and down);
+                                   NULL for none */
     void *prof_event_end;       /* optional hipEvent_t recorded just after it */
 } moe_ffn_args;
 
