@@ -65,8 +65,10 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 {
     using V = typename Tr::V;
     constexpr int epl = Tr::kEpl;
-    // rows per batch: 4 vectors of weights per lane per batch, two batches in flight
-    constexpr int UR = 4 / NSW < 1 ? 1 : 4 / NSW;
+    // rows per batch: 8 vectors of weights per lane per batch, two batches in
+    // flight (one token leaves the registers for twice the projection's
+    // batches: the gate's 32 rows take two memory round trips instead of four)
+    constexpr int UR = 8 / NSW < 1 ? 1 : 8 / NSW;
     constexpr int NB = kChunk / UR;
     static_assert(NB % 2 == 0, "ping-pong needs an even batch count");
     constexpr int rowV = NW * NSW * kWave;  // 16-byte vectors per row

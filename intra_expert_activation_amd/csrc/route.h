@@ -19,19 +19,19 @@ __device__ __forceinline__ float slot_weight(float ev, float sel_sum, float deno
     return isnan(denom) ? denom : ev / sel_sum;
 }
 
-// Routes token t with one wavefront: lane k < K ends with the expert id and
-// the weight of slot k.
-__device__ __forceinline__ void route_token(const float *__restrict__ logits, int t, int E, int K, int renorm,
-                                            int &id, float &wt)
+// Routes token t with one wavefront, KP logits per lane (E <= 64 * KP): lane
+// k < K ends with the expert id and the weight of slot k.
+template <int KP>
+__device__ __forceinline__ void route_token_kp(const float *__restrict__ logits, int t, int E, int K, int renorm,
+                                               int &id, float &wt)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const float *l = logits + (size_t)t * E;
-    constexpr int kPer = kMaxExperts / kWave;
-    float v[kPer];      // ranking value (NaN ranks as -inf)
-    float raw[kPer];    // logit as given
+    float v[KP];        // ranking value (NaN ranks as -inf)
+    float raw[KP];      // logit as given
     uint32_t avail = 0; // bit i: expert lane + 64 i is present and not yet chosen
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
+    for (int i = 0; i < KP; ++i) {
         const int e = lane + kWave * i;
         raw[i] = e < E ? l[e] : 0.f;
         v[i] = (e < E && !isnan(raw[i])) ? raw[i] : -INFINITY;
@@ -40,12 +40,12 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
     // maximum over the non-NaN logits, for a range-safe softmax
     float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
+    for (int i = 0; i < KP; ++i)
         if ((avail >> i) & 1u) m = fmaxf(m, v[i]);
     m = wave_max(m);
     float denom = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
+    for (int i = 0; i < KP; ++i)
         if ((avail >> i) & 1u) denom += expf(raw[i] - m);
     denom = wave_sum_all(denom);
 
@@ -54,22 +54,22 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
     float sel_sum = 0.f;
     for (int k = 0; k < K; ++k) {
         // lane-local best available expert (ascending ids: ties keep the lower)
-        float bv = -INFINITY, braw = 0.f;
+        float bv = -INFINITY;
         int bid = 0x7fffffff;
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
+        for (int i = 0; i < KP; ++i) {
             if (((avail >> i) & 1u) && (bid == 0x7fffffff || v[i] > bv)) {
                 bv = v[i];
-                braw = raw[i];
                 bid = lane + kWave * i;
             }
         }
         // wavefront arg-max: the largest value, then the lowest id holding it
         const float top = wave_max(bid == 0x7fffffff ? -INFINITY : bv);
         const int win = wave_min((bid != 0x7fffffff && bv == top) ? bid : 0x7fffffff);
-        const float wraw = __shfl(braw, win & (kWave - 1), kWave);  // the chosen logit, as given
         if ((win & (kWave - 1)) == lane) avail &= ~(1u << (win / kWave));
-        const float ev = expf(wraw - m);
+        // exp of the chosen logit: its ranking value is the logit itself unless
+        // the logit is NaN, and then the denominator is NaN and so is every weight
+        const float ev = expf(top - m);
         if (lane == k) {
             chosen_e = ev;
             chosen_id = win;
@@ -78,6 +78,17 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
     }
     id = chosen_id;
     wt = slot_weight(chosen_e, sel_sum, denom, renorm);
+}
+
+// Routes token t with one wavefront (E <= 512): lane k < K ends with the
+// expert id and the weight of slot k.  E decides how many logits a lane holds.
+__device__ __forceinline__ void route_token(const float *__restrict__ logits, int t, int E, int K, int renorm,
+                                            int &id, float &wt)
+{
+    if (E <= kWave) route_token_kp<1>(logits, t, E, K, renorm, id, wt);
+    else if (E <= 2 * kWave) route_token_kp<2>(logits, t, E, K, renorm, id, wt);
+    else if (E <= 4 * kWave) route_token_kp<4>(logits, t, E, K, renorm, id, wt);
+    else route_token_kp<kMaxExperts / kWave>(logits, t, E, K, renorm, id, wt);
 }
 
 }  // namespace moe
