@@ -52,6 +52,7 @@ def _load():
         lib.oracle_moe.argtypes = [i32] * 9 + [vp] * 9 + [i32, vp] + [vp] * 7 + [i32]
         lib.oracle_moe.restype = i32
         lib.oracle_calibrate.argtypes = [i32] * 8 + [vp] * 4 + [ctypes.c_double, i32, vp, i32]
+        lib.oracle_topk_mask.argtypes = [i32, i32, vp, vp, i32, vp]
         lib.oracle_calibrate.restype = i32
         _lib = lib
     return _lib
@@ -171,3 +172,33 @@ def calibrate(layer: dict, x_calib: np.ndarray, logits_calib: np.ndarray, q: flo
     if rc:
         raise ValueError(f"oracle_calibrate: invalid arguments (rc={rc})")
     return tau
+
+
+def topk_masks(scores: np.ndarray, rows: np.ndarray, budget: int) -> np.ndarray:
+    """Top-k neuron masks [..., W] uint32 from scores a [..., Imax] (oracle_moe's
+    ``want_scores`` output) and each pair's expert row count ``rows`` [...]:
+    the ``budget`` largest |a| of a pair are active (see oracle_topk_mask)."""
+    lib = _load()
+    sc = np.ascontiguousarray(scores, dtype=np.float64)
+    lead, Imax = sc.shape[:-1], sc.shape[-1]
+    rw = np.ascontiguousarray(np.broadcast_to(np.asarray(rows, np.int32), lead))
+    n = int(np.prod(lead)) if lead else 1
+    W = (Imax + 31) // 32
+    out = np.zeros(lead + (W,), np.uint32)
+    if lib.oracle_topk_mask(n, Imax, _ptr(sc), _ptr(rw), int(budget), _ptr(out)):
+        raise ValueError("oracle_topk_mask: invalid arguments")
+    return out
+
+
+def moe_topk(layer: dict, x: np.ndarray, logits: np.ndarray, budget: int,
+             threads: int | None = None) -> OracleResult:
+    """The layer with per-pair top-k neuron selection instead of the threshold:
+    the scores of every pair (the dense pass), their top-``budget`` masks, then
+    the layer under those masks.  ``scores`` of the result are the dense pass's."""
+    E, S = layer["E"], layer.get("S", 0)
+    d = moe(layer, x, logits, 0.0, dense=True, want_scores=True, threads=threads)
+    exp = np.concatenate([d.ids, np.broadcast_to(E + np.arange(S, dtype=np.int32), (d.ids.shape[0], S))], axis=1)
+    rows = np.where(exp < E, layer["I"], layer.get("I_shared", 0))
+    m = topk_masks(d.scores, rows, budget)
+    o = moe(layer, x, logits, 0.0, force_mask=m, threads=threads)
+    return OracleResult(o.y, o.mask_bits, d.scores, o.union_idx, o.union_cnt, o.ids, o.w)

@@ -378,3 +378,63 @@ int oracle_calibrate(int Tc, int H, int E, int I, int K, int S, int Is,
     free(wts);
     return 0;
 }
+
+/* ----------------------------------------------------------------------- */
+/* The top-k alternative to the threshold.  [TS] Methodology, Activation    */
+/* Masking: the method masks with one elementwise threshold pass instead of */
+/* selecting the top-k activations per token.  For comparison, this takes   */
+/* that alternative literally: for each (token, slot) pair the `budget`     */
+/* neurons of largest |a_j| are active.  READING (the pages give no tie     */
+/* rule): a NaN score ranks first, as the threshold counts NaN as active,   */
+/* and equal scores go to the lower neuron index.  An expert with at most   */
+/* `budget` rows keeps them all.                                            */
+/* ----------------------------------------------------------------------- */
+typedef struct {
+    double mag;  /* |a_j| */
+    int j;
+} ranked_neuron;
+
+/* Descending |a| with NaN first; equal magnitudes by ascending j. */
+static int cmp_ranked(const void *pa, const void *pb)
+{
+    const ranked_neuron *a = (const ranked_neuron *)pa, *b = (const ranked_neuron *)pb;
+    const int na = isnan(a->mag), nb = isnan(b->mag);
+    if (na != nb) return nb - na;
+    if (!na) {
+        if (a->mag > b->mag) return -1;
+        if (a->mag < b->mag) return 1;
+    }
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+/*
+ * oracle_topk_mask -- mask words [npairs, W] (W = ceil(Imax/32)) from the
+ * scores a [npairs, Imax] of oracle_moe; rows[p] is the row count of pair p's
+ * expert.  Returns 0, or 1 for invalid arguments.
+ */
+int oracle_topk_mask(int npairs, int Imax, const double *scores, const int32_t *rows, int budget,
+                     uint32_t *mask)
+{
+    if (npairs < 0 || Imax <= 0 || budget < 0 || !scores || !rows || !mask) return 1;
+    const int W = (Imax + 31) / 32;
+    ranked_neuron *v = (ranked_neuron *)malloc(sizeof(ranked_neuron) * (size_t)Imax);
+    if (!v) return 1;
+    for (int p = 0; p < npairs; ++p) {
+        uint32_t *m = mask + (size_t)p * W;
+        for (int w = 0; w < W; ++w) m[w] = 0u;
+        const int n = rows[p];
+        if (n < 0 || n > Imax) {
+            free(v);
+            return 1;
+        }
+        for (int j = 0; j < n; ++j) {
+            v[j].mag = fabs(scores[(size_t)p * Imax + j]);
+            v[j].j = j;
+        }
+        qsort(v, (size_t)n, sizeof(ranked_neuron), cmp_ranked);
+        const int keep = budget < n ? budget : n;
+        for (int i = 0; i < keep; ++i) m[v[i].j / 32] |= 1u << (v[i].j % 32);
+    }
+    free(v);
+    return 0;
+}

@@ -368,3 +368,110 @@ def test_calibration_monotone_and_per_expert():
             v = np.abs(r.scores[rows, 0, :]).ravel()
             kappa = math.floor(float(np.float32(0.5)) * v.size)
             assert per[e] == np.partition(v, kappa)[kappa]
+
+
+# --------------------------------------------------------------------------
+# The top-k alternative to the threshold ([TS] Methodology, Activation
+# Masking contrasts the two): per-pair selection of the budget largest |a|
+# --------------------------------------------------------------------------
+def _bits(mask, rows):
+    return [int(j) for j in np.flatnonzero(_unpack(np.asarray(mask, np.uint32), rows))]
+
+
+def test_topk_hand_example():
+    # |a| = 0.5, 2.0, NaN, 0.5, 1.0: NaN first, then 2.0, 1.0, then the tie at
+    # 0.5 goes to the lower index 0
+    s = np.array([[0.5, -2.0, np.nan, 0.5, 1.0]])
+    assert _bits(oracle.topk_masks(s, [5], 0)[0], 5) == []
+    assert _bits(oracle.topk_masks(s, [5], 1)[0], 5) == [2]
+    assert _bits(oracle.topk_masks(s, [5], 3)[0], 5) == [1, 2, 4]
+    assert _bits(oracle.topk_masks(s, [5], 4)[0], 5) == [0, 1, 2, 4]
+    assert _bits(oracle.topk_masks(s, [5], 9)[0], 5) == [0, 1, 2, 3, 4]
+    # rows beyond the pair's expert are never chosen
+    assert _bits(oracle.topk_masks(s, [3], 9)[0], 5) == [0, 1, 2]
+
+
+def test_topk_brute_force():
+    rng = np.random.default_rng(11)
+    s = np.round(rng.standard_normal((3, 4, 70)) * 4) / 4  # many exact ties
+    rows = np.array([70, 40, 70, 33])
+    for budget in (0, 1, 17, 33, 40, 69, 70, 100):
+        m = oracle.topk_masks(s, rows, budget)
+        for idx in np.ndindex(3, 4):
+            n = rows[idx[1]]
+            on = _unpack(m[idx], 70)
+            assert on.sum() == min(budget, n) and not on[n:].any()
+            mag = np.abs(s[idx][:n])
+            act, off = np.flatnonzero(on[:n]), np.flatnonzero(~on[:n])
+            if len(act) and len(off):
+                assert mag[act].min() >= mag[off].max()
+                # equal magnitudes across the boundary: the active ones are the lower rows
+                edge = mag[act].min()
+                if edge == mag[off].max():
+                    assert np.flatnonzero(on[:n] & (mag == edge)).max() < np.flatnonzero(~on[:n] & (mag == edge)).min()
+
+
+def test_topk_equals_threshold_at_the_kth_score():
+    # with distinct scores, keeping the top k is thresholding at the k-th
+    # largest |a| (numpy sort), since the threshold keeps |a| >= tau
+    rng = np.random.default_rng(12)
+    s = rng.standard_normal((5, 96))
+    for budget in (1, 10, 50, 95):
+        m = oracle.topk_masks(s, 96, budget)
+        tau = -np.sort(-np.abs(s), axis=1)[:, budget - 1:budget]
+        np.testing.assert_array_equal(_unpack(m, 96), ~(np.abs(s) < tau))
+
+
+def test_topk_layer_limits():
+    L, x, logits = _layer(H=24, E=5, I=40, K=2, S=1, Is=32, dtype="bf16")
+    dense = oracle.moe(L, x, logits, 0.0, dense=True)
+    full = oracle.moe_topk(L, x, logits, 40)
+    np.testing.assert_array_equal(full.y, dense.y)
+    assert (oracle.moe_topk(L, x, logits, 0).y == 0).all()
+    # a budget keeps exactly that many neurons of every pair
+    k7 = oracle.moe_topk(L, x, logits, 7)
+    cnt = _unpack(k7.mask_bits, 40).sum(axis=-1)
+    assert (cnt == 7).all()
+    # and the layer output is the textbook layer under exactly those masks
+    np.testing.assert_allclose(k7.y, _textbook_forced(L, x, logits, k7.mask_bits), rtol=1e-12, atol=1e-12)
+
+
+def _textbook_forced(L, x, logits, mask_bits):
+    """The layer with given per-(token, slot) masks, from library routines:
+    float64 matmuls, torch's SiLU, scipy's softmax and a stable argsort."""
+    dt = L["dtype"]
+    X = torch.from_numpy(_f64(x, dt))
+    T, E, K, S = x.shape[0], L["E"], L["K"], L["S"]
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :K]
+    Imax = max(L["I"], L["I_shared"]) if S else L["I"]
+    M = _unpack(mask_bits, Imax)
+    y = np.zeros((T, L["H"]))
+    for t in range(T):
+        sel = p[t, order[t]]
+        if L["renormalize"]:
+            sel = sel / sel.sum()
+        for k in range(K + S):
+            e = order[t, k] if k < K else E + k - K
+            pre, i = ("w_", e) if e < E else ("ws_", e - E)
+            rows = L["I"] if e < E else L["I_shared"]
+            Wg = torch.from_numpy(_f64(L[pre + "gate"][i], dt))
+            Wu = torch.from_numpy(_f64(L[pre + "up"][i], dt))
+            Wd = torch.from_numpy(_f64(L[pre + "down"][i], dt))
+            a = torch.nn.functional.silu(Wg @ X[t])
+            hv = torch.where(torch.from_numpy(M[t, k, :rows]), a * (Wu @ X[t]), torch.zeros_like(a))
+            y[t] += (sel[k] if k < K else 1.0) * (hv @ Wd).numpy()
+    return y
+
+
+def test_force_mask_equals_textbook():
+    # the oracle's forced-mask path (used for the top-k variant and for the
+    # parity checks) against the textbook layer under random masks
+    L, x, logits = _layer(H=24, E=6, I=48, K=3, S=2, Is=64, renorm=0, dtype="bf16")
+    rng = np.random.default_rng(13)
+    m = rng.random((x.shape[0], L["K"] + 2, 64)) < 0.3
+    m[:, :L["K"], 48:] = False
+    packed = np.packbits(m, axis=-1, bitorder="little").view(np.uint32)
+    r = oracle.moe(L, x, logits, 0.0, force_mask=packed)
+    np.testing.assert_allclose(r.y, _textbook_forced(L, x, logits, packed), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(r.mask_bits, packed)
