@@ -60,8 +60,12 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* MOE_SPARSE applies the threshold mask; MOE_DENSE computes the ordinary
  * dense SwiGLU MoE layer (every neuron active) and serves as the baseline the
  * sparse execution is compared with (Technical Summary, Results: layer
- * speedup over the dense pipeline). */
-typedef enum { MOE_SPARSE = 0, MOE_DENSE = 1 } moe_mode;
+ * speedup over the dense pipeline).  MOE_TOPK is the alternative the
+ * threshold pass is contrasted with (Technical Summary, Methodology,
+ * Activation Masking: a top-k selection instead of one elementwise pass):
+ * for every (token, slot) pair the neuron_budget neurons with the largest
+ * |a_j| are active, whatever their values. */
+typedef enum { MOE_SPARSE = 0, MOE_DENSE = 1, MOE_TOPK = 2 } moe_mode;
 
 /*
  * Layer shape.
@@ -142,6 +146,11 @@ typedef struct {
                                    kernel that also runs routing and down);
                                    NULL for none */
     void *prof_event_end;       /* optional hipEvent_t recorded just after it */
+    int32_t neuron_budget;      /* MOE_TOPK only: active neurons per (token,
+                                   slot) pair, >= 0; an expert with fewer rows
+                                   keeps all of them.  The order is |a_j|
+                                   descending, a NaN score first, equal scores
+                                   by ascending j.  tau is not read. */
 } moe_ffn_args;
 
 /*

@@ -19,7 +19,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
 {
     if (!s || !p) return MOE_ERR_INVALID_ARG;
     const bool calib = calib_tokens > 0;
-    if (!calib && mode != MOE_SPARSE && mode != MOE_DENSE) return MOE_ERR_INVALID_ARG;
+    if (!calib && mode != MOE_SPARSE && mode != MOE_DENSE && mode != MOE_TOPK) return MOE_ERR_INVALID_ARG;
     const int T = calib ? calib_tokens : s->T;
     if (T < 0 || s->H <= 0 || s->E <= 0 || s->I <= 0 || s->K <= 0 || s->K > s->E || s->S < 0)
         return MOE_ERR_INVALID_ARG;
@@ -105,7 +105,8 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->max_items = 0;
     p->max_pairs = 0;
     const int nm = kMfmaMinPairs;
-    if (!calib && p->dtype == MOE_BF16 && T >= nm) {
+    p->topk = (!calib && mode == MOE_TOPK) ? 1 : 0;
+    if (!calib && !p->topk && p->dtype == MOE_BF16 && T >= nm) {
         p->nm = nm;
         p->use_mfma = 1;
         // sum over experts of ceil(n_e / 64) <= A/64 + (number of such experts)
@@ -127,7 +128,8 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // per expert) T 2: 122 -> 126, so it keeps the grouped path from T 2.
     {
         const size_t gate_bytes = (size_t)p->Imax * p->H * (p->dtype == MOE_BF16 ? 2 : 4);
-        p->fused = !calib && T >= 1 && (T == 1 || (T <= kFusedMaxT && gate_bytes <= ((size_t)16 << 20))) ? 1 : 0;
+        p->fused = !calib && !p->topk && T >= 1 && (T == 1 || (T <= kFusedMaxT && gate_bytes <= ((size_t)16 << 20)))
+                       ? 1 : 0;
     }
 
     // workspace layout
@@ -162,7 +164,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);
     p->off_hlo = take(blocks * 64 * 64 * 2);
-    p->off_mw = take(p->fused ? (size_t)p->P * p->W * 4 : 0);
+    p->off_mw = take((p->fused || p->topk) ? (size_t)p->P * p->W * 4 : 0);
     p->total = o;
     return MOE_OK;
 }
@@ -236,6 +238,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
         return MOE_ERR_INVALID_ARG;
     if (pl.S > 0 && (!a->ws_gate || !a->ws_up || !a->ws_down)) return MOE_ERR_INVALID_ARG;
     if (mode == MOE_SPARSE && !a->tau) return MOE_ERR_INVALID_ARG;
+    if (mode == MOE_TOPK && a->neuron_budget < 0) return MOE_ERR_INVALID_ARG;
     const void *a16[] = {a->x, a->w_gate, a->w_up, a->w_down, a->y};
     for (const void *ptr : a16)
         if (!aligned(ptr, 16)) return MOE_ERR_INVALID_ARG;
@@ -326,7 +329,21 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     // the events bracket the expert projection (gate, score, mask, up) of both paths
     if (a->prof_event_begin && hipEventRecord((hipEvent_t)a->prof_event_begin, stream) != hipSuccess)
         return MOE_ERR_HIP;
-    if (launch_proj(pl, pp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    if (pl.topk) {
+        // every pair's gate scores, the per-pair selection of the budget
+        // largest, then the projection under those masks (up and h; the gate
+        // is not read again)
+        if (launch_proj(pl, pp, mp, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
+        TopkParams tp{};
+        tp.a = h; tp.counts = counts; tp.offsets = offsets; tp.pair_tok = pair_tok; tp.pair_slot = pair_slot;
+        tp.ids = ids; tp.pmask = ws_at<uint32_t>(ws, pl.off_mw);
+        tp.E = pl.E; tp.I = pl.I; tp.Is = pl.Is; tp.K = pl.K; tp.A = pl.A; tp.W = pl.W; tp.budget = a->neuron_budget;
+        if (launch_topk_select(pl, tp, stream) != hipSuccess) return MOE_ERR_HIP;
+        pp.pmask = tp.pmask;
+        if (launch_proj(pl, pp, mp, kModeMasked, stream) != hipSuccess) return MOE_ERR_HIP;
+    } else if (launch_proj(pl, pp, mp, mode, stream) != hipSuccess) {
+        return MOE_ERR_HIP;
+    }
     if (a->prof_event_end && hipEventRecord((hipEvent_t)a->prof_event_end, stream) != hipSuccess)
         return MOE_ERR_HIP;
 
@@ -339,7 +356,8 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
     dp.W = pl.W; dp.Imax = pl.Imax; dp.NCT = pl.NCT; dp.KMAX = pl.KMAX;
     dp.nm = pl.nm;
-    if (launch_down(pl, dp, mp, mode, stream) != hipSuccess) return MOE_ERR_HIP;
+    // the top-k masks and unions are consumed like the threshold's
+    if (launch_down(pl, dp, mp, pl.topk ? MOE_SPARSE : mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
     cp.partial = partial; cp.topk_w = w; cp.npc = npc; cp.y = a->y;

@@ -53,6 +53,7 @@ struct Plan {
     // one-launch decode path (small batches): every (pair, 32-row chunk)
     // runs routing, gate, mask, up and down; a second launch combines
     int fused;
+    int topk;        // MOE_TOPK: scores, per-pair selection, then the masked projection
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
@@ -97,6 +98,7 @@ struct ProjParams {
     const float *tau;
     const int32_t *hdr, *counts, *offsets, *touched, *pair_tok, *pair_slot;
     const int32_t *order; // GroupParams::order: the order in which workgroups take the experts
+    const uint32_t *pmask;// kModeMasked: mask words by grouped pair [P, W]
     float *h;             // per-expert blocks [rows][n_e] (fp32)
     uint32_t *mask_bits;  // optional output [T,slots,W]
     uint32_t *union_words;// [EX,W]
@@ -163,6 +165,14 @@ struct FusedParams {
     int T, H, E, I, Is, S, K, slots, P, C, W, Imax, renorm;
 };
 
+// Per-pair top-k neuron selection (MOE_TOPK).
+struct TopkParams {
+    const float *a;       // scores as ProjParams::h after kModeScore
+    const int32_t *counts, *offsets, *pair_tok, *pair_slot, *ids;
+    uint32_t *pmask;      // out [P, W] by grouped pair
+    int E, I, Is, K, A, W, budget;
+};
+
 struct SelectParams {
     const float *scores;  // |SiLU| per (pair, neuron), expert blocks as ProjParams::h
     const int32_t *counts, *offsets;
@@ -179,14 +189,18 @@ hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, in
 // Routing then grouping of gp.T tokens (ids/w: the routing outputs, also gp.ids).
 hipError_t launch_route_group(const float *logits, int renorm, int32_t *ids, float *w, const GroupParams &gp,
                               hipStream_t stream);
-// mode: MOE_SPARSE, MOE_DENSE, or kModeScore (calibration scores)
-constexpr int kModeScore = 2;
+// mode: MOE_SPARSE, MOE_DENSE, kModeScore (gate scores a = SiLU(g) of every
+// pair and neuron, written where h goes) or kModeMasked (the masks come from
+// pmask and the scores from h's place; the gate is not read again)
+constexpr int kModeScore = 3;
+constexpr int kModeMasked = 4;
 // MFMA workgroups (experts with >= nm pairs) run in the same launch for bf16
 // layers with 256-thread GEMV workgroups, else in a second launch.
 hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t stream);
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
+hipError_t launch_topk_select(const Plan &pl, const TopkParams &tp, hipStream_t stream);
 hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_down_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
 // The one-launch decode path and its combine; the events (optional) bracket

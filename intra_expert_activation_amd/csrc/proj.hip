@@ -72,7 +72,8 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     // scheduling barriers keep each batch's loads ahead of the other batch's
     // arithmetic.
     V bufA[UR][NSW], bufB[UR][NSW];
-    load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);  // weights first: they do not wait for the tokens
+    if constexpr (MODE != kModeMasked)
+        load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);  // weights first: they do not wait for the tokens
 
     // this wavefront's slice of the tile's hidden states
     V xr[TT][NSW];
@@ -86,7 +87,7 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     if (threadIdx.x == 0) L.act = 0u;
 
     // ---- gate: 32 rows in NB batches -----------------------------------------
-    {
+    if constexpr (MODE != kModeMasked) {
         int b = 0;
 #pragma unroll 1
         for (; b + 2 < NB; b += 2) {
@@ -109,12 +110,22 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     // ---- scores, masks, active rows -----------------------------------------
     for (int i = threadIdx.x; i < kChunk * TT; i += NW * kWave) {
         const int r = i / TT, t = i - r * TT;
+        if constexpr (MODE == kModeMasked) {  // the scores and masks of an earlier pass
+            if (t < nt) {
+                L.a[r][t] = hb[(size_t)r * n + t0 + t];
+                if ((p.pmask[(size_t)(off + t0 + t) * p.W + (r0 >> 5)] >> r) & 1u) {
+                    atomicOr(&L.mask[t], 1u << r);
+                    atomicOr(&L.act, 1u << r);
+                }
+            }
+            continue;
+        }
         float g = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) g += s_part[w][r][t];
         const float a = silu(g);
         if (MODE == kModeScore) {
-            if (t < nt) hb[(size_t)r * n + t0 + t] = fabsf(a);
+            if (t < nt) hb[(size_t)r * n + t0 + t] = a;  // signed: |a| is the score
         } else {
             L.a[r][t] = a;
             const bool m = (t < nt) && (MODE == MOE_DENSE || !(fabsf(a) < tau));
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams m
     if ((int)blockIdx.x >= mfma_blocks) {
         proj_gemv<BF16, 4, NSW, TTMAX, MODE>(p, S.gemv, blockIdx.x - mfma_blocks);
     } else {
-        if constexpr (MODE != kModeScore) mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x);
+        if constexpr (MODE == MOE_SPARSE || MODE == MOE_DENSE) mfma_proj_body<MODE>(mp, S.mfma, blockIdx.x);
     }
 }
 
@@ -275,7 +286,7 @@ static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
 template <class Tr, int NW, int NSW, int TT, int MODE>
 static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, hipStream_t st)
 {
-    const bool mfma = MODE != kModeScore && pl.use_mfma;
+    const bool mfma = (MODE == MOE_SPARSE || MODE == MOE_DENSE) && pl.use_mfma;
     // one 16-byte vector per lane per row only: with more, the merged kernel's
     // GEMV body does not fit 3 workgroups per CU, and the MFMA tiles get a
     // launch of their own
@@ -300,6 +311,7 @@ static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, const Mfma
 {
     if (mode == MOE_SPARSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_SPARSE>(pl, pp, mp, st);
     if (mode == MOE_DENSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_DENSE>(pl, pp, mp, st);
+    if (mode == kModeMasked) return launch_proj_m<Tr, NW, NSW, TT, kModeMasked>(pl, pp, mp, st);
     return launch_proj_m<Tr, NW, NSW, TT, kModeScore>(pl, pp, mp, st);
 }
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoesparse.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SPARSE, MOE_DENSE = 0, 1
+MOE_SPARSE, MOE_DENSE, MOE_TOPK = 0, 1, 2
 
 # every symbol include/moe_sparse.h declares
 EXPORTS = (
@@ -37,7 +37,8 @@ class MoeFfnArgs(ctypes.Structure):
         "x", "router_logits", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down", "tau",
         "y", "mask_bits", "union_idx", "union_cnt", "topk_ids", "topk_w", "workspace")] + [
         ("workspace_bytes", ctypes.c_size_t),
-        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p)]
+        ("prof_event_begin", ctypes.c_void_p), ("prof_event_end", ctypes.c_void_p),
+        ("neuron_budget", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -143,9 +144,11 @@ def route_topk(logits: torch.Tensor, K: int, renormalize: bool = True):
 
 def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, renormalize=True,
                       shared=None, mode=MOE_SPARSE, want_masks=True, out=None, workspace=None,
-                      prof_events=None):
+                      prof_events=None, neuron_budget=0):
     """One MoE layer forward.  ``shared`` = (ws_gate, ws_up, ws_down) or None.
 
+    ``mode`` MOE_TOPK keeps the ``neuron_budget`` largest |SiLU(gate)| neurons
+    of every (token, slot) pair instead of thresholding (``tau`` unused).
     Returns a dict with ``y`` [T,H] fp32 and, when ``want_masks``, ``mask_bits``
     [T,K+S,W] int32 (bit patterns), ``union_idx`` [E+S,Imax], ``union_cnt`` [E+S],
     ``topk_ids`` and ``topk_w``.  ``out`` may supply preallocated outputs.
@@ -180,6 +183,7 @@ def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, re
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     if prof_events is not None:
         a.prof_event_begin, a.prof_event_end = prof_events
+    a.neuron_budget = int(neuron_budget)
     _check(lib().moe_sparse_expert_ffn(ctypes.byref(shape), int(mode), ctypes.byref(a), _stream(dev)),
            "moe_sparse_expert_ffn")
     return o

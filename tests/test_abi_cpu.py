@@ -118,6 +118,19 @@ def test_ffn_tau_required_only_when_sparse(L):
     assert _ffn(_shape(), a, moe.MOE_DENSE) == moe.MOE_ERR_WORKSPACE
 
 
+def test_ffn_topk_mode(L):
+    # the top-k variant needs no tau; a negative budget is rejected before any HIP call
+    assert _ws(_shape(), moe.MOE_TOPK)[0] == moe.MOE_OK
+    a = _args(tau=None)
+    a.neuron_budget = -1
+    assert _ffn(_shape(), a, moe.MOE_TOPK) == moe.MOE_ERR_INVALID_ARG
+    a = _args(tau=None)
+    a.neuron_budget = 115
+    a.workspace_bytes = 16
+    assert _ffn(_shape(), a, moe.MOE_TOPK) == moe.MOE_ERR_WORKSPACE
+    assert _ws(_shape(), 3)[0] == moe.MOE_ERR_INVALID_ARG
+
+
 def test_ffn_shared_pointers_required(L):
     assert _ffn(_shape(S=2, I_shared=768), _args()) == moe.MOE_ERR_INVALID_ARG
 

@@ -12,7 +12,8 @@ import torch
 import oracle
 from intra_expert_activation_amd import moe, synth
 
-from parity_util import cached_layer, check_layer, dev_tensor, gpu_ffn, layer_to_device, rel_l2, unpack_bits
+from parity_util import (cached_layer, check_layer, dev_tensor, gpu_ffn, layer_to_device, pack_bits, rel_l2,
+                         slot_experts, unpack_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -366,6 +367,53 @@ def test_single_token_edge_cases():
     again = gpu_ffn(DL, x1, l1, tau)
     for k in full:
         assert np.array_equal(full[k], again[k]), k
+
+
+# ---------------------------------------------------------------------------
+# The top-k alternative (MOE_TOPK): for every (token, slot) pair the budget
+# neurons with the largest |a| are active
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,T,frac", [(1, 16, 0.2), (2, 64, 0.15), (2, 5, 0.15), (4, 32, 0.15), (2, 40, 1.0),
+                                        (4, 3, 0.02)])
+def test_topk_variant(cfg, T, frac):
+    c, L = cached_layer(cfg)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    E, S, K = L["E"], L["S"], L["K"]
+    budget = max(1, int(round(frac * L["I"])))
+    g = gpu_ffn(DL, x, logits, None, mode=moe.MOE_TOPK, neuron_budget=budget)
+    o = oracle.moe_topk(L, x, logits, budget)
+    np.testing.assert_array_equal(g["topk_ids"], o.ids)
+    Imax = max(L["I"], L["I_shared"]) if S else L["I"]
+    W = Imax // 32
+    exp = slot_experts(o.ids, E, S)
+    rows = np.where(exp < E, L["I"], L["I_shared"] if S else 0)
+    gm = unpack_bits(g["mask_bits"], W * 32)
+    om = unpack_bits(o.mask_bits, W * 32)
+    # exactly the budget (or every row) per pair, none past the expert's rows
+    assert (gm.sum(axis=-1) == np.minimum(budget, rows)).all()
+    assert not (gm & ~(np.arange(W * 32)[None, None, :] < rows[..., None])).any()
+    # the selections differ only at the boundary: scores within 1e-3 of the
+    # pair's budget-th largest |a| (the GPU ranks fp32 scores)
+    mag = np.abs(np.nan_to_num(o.scores, nan=np.inf))
+    kth = np.zeros(rows.shape)
+    for idx in np.ndindex(rows.shape):
+        srt = -np.sort(-mag[idx][:rows[idx]])
+        kth[idx] = srt[min(budget, rows[idx]) - 1]
+    band = np.zeros_like(gm)
+    band[..., :Imax] = np.abs(mag - kth[..., None]) <= 1e-3 * kth[..., None]
+    assert not ((gm != om) & ~band).any(), int(((gm != om) & ~band).sum())
+    # the layer under the GPU's own masks
+    o2 = oracle.moe(L, x, logits, 0.0, force_mask=pack_bits(gm[..., :Imax], W))
+    tol = TOL_F32 if L["dtype"] == "f32" else TOL_BF16
+    assert rel_l2(g["y"], o2.y) <= tol
+    # unions: the OR of the GPU's masks over each expert's pairs
+    for e in range(E + S):
+        sel = exp == e
+        r = L["I"] if e < E else L["I_shared"]
+        want = np.flatnonzero(gm[sel].any(axis=0)[:r]) if sel.any() else np.array([], int)
+        assert g["union_cnt"][e] == len(want)
+        np.testing.assert_array_equal(g["union_idx"][e, :len(want)], want)
 
 
 # ---------------------------------------------------------------------------
