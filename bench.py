@@ -15,8 +15,9 @@ per graph, and with eager launches, is reported beside it.
 
 Prints ONE JSON line (rank 0) with the headline tokens/s, the roofline of the
 dominant kernel (expert projection: gate, score, mask, up), the speedup over
-the library's own dense mode, a batch sweep, and the CPU oracle's throughput on
-a bounded sample of the same workload.
+the library's own dense mode, a batch sweep, the time of the top-k neuron
+selection variant at the same sparsity, and the CPU oracle's throughput on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -150,7 +151,7 @@ def main():
                     topk_ids=torch.empty((Tb, K), dtype=torch.int32, device=dev),
                     topk_w=torch.empty((Tb, K), dtype=torch.float32, device=dev))
 
-    def run(Tb, mode, steps, warmup, kernel_timing, graph, chain=True):
+    def run(Tb, mode, steps, warmup, kernel_timing, graph, chain=True, budget=0):
         bs = batches(Tb)
         outs = [make_outputs(Tb) for _ in range(rotate)]
         shape = moe.layer_shape(bs[0][0], Wg, K, renorm, shared[0] if S else None)
@@ -159,7 +160,7 @@ def main():
         def call(r, ev=None):
             x, lg = bs[r]
             moe.sparse_expert_ffn(x, lg, Wg, Wu, Wd, tau, K=K, renormalize=renorm, shared=shared, mode=mode,
-                                  out=outs[r], workspace=ws, prof_events=ev)
+                                  out=outs[r], workspace=ws, prof_events=ev, neuron_budget=budget)
 
         # per-batch algorithmic bytes and flops from the returned unions
         for r in range(rotate):
@@ -171,7 +172,7 @@ def main():
             ne = np.bincount(outs[r]["topk_ids"].cpu().numpy().ravel(), minlength=E + S).astype(np.int64)
             ne[E:] = Tb
             t = ne > 0
-            u = ucnt if mode == moe.MOE_SPARSE else rows
+            u = rows if mode == moe.MOE_DENSE else ucnt
             gate_rows, union_rows = int(rows[t].sum()), int(u[t].sum())
             proj_bytes.append((gate_rows + union_rows) * H * 2 + Tb * H * 2)
             call_bytes.append((gate_rows + 2 * union_rows) * H * 2 + Tb * H * 2 + Tb * E * 4 + Tb * H * 4)
@@ -271,6 +272,18 @@ def main():
                           hbm_frac_call=round(sp["call_gbs"] / HBM_PEAK_GBS, 4),
                           union_fraction=round(sp["union_fraction"], 4)))
 
+    # the top-k alternative at the same sparsity: the budget largest |a| of
+    # every pair instead of the threshold (a score pass, a per-pair selection
+    # and a masked projection in place of the one fused threshold pass)
+    topk = None
+    if T < 1024:
+        budget = int(round((1.0 - args.q) * I))
+        tk = run(T, moe.MOE_TOPK, args.steps, args.warmup, kernel_timing=False, graph=use_graph, budget=budget)
+        topk = dict(neuron_budget=budget, ms_per_step=round(tk["ms_per_step"], 5),
+                    time_vs_threshold=round(tk["ms_per_step"] / head_g["ms_per_step"], 3),
+                    speedup_vs_dense=round(dense_g["ms_per_step"] / tk["ms_per_step"], 3),
+                    union_fraction=round(tk["union_fraction"], 4))
+
     best = head_g if head_g["ms_per_step"] < head["ms_per_step"] else head
     traffic = None
     if args.workload == "decode" and T == 64 and os.path.exists(TRAFFIC_FILE):
@@ -318,6 +331,7 @@ def main():
         "call_tflops": round(head_g["call_tflops"], 1),
         "union_fraction": round(head["union_fraction"], 4),
         "sweep": sweep,
+        "topk_variant": topk,
         "setup_s": round(gen_s, 1),
     }
 
