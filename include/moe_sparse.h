@@ -141,9 +141,10 @@ typedef struct {
     void *prof_event_begin;     /* optional hipEvent_t recorded on the stream
                                    just before the expert projection kernel
                                    (gate/score/mask/up; for batches of one
-                                   token, and of up to 8 tokens when an
-                                   expert's gate holds at most 16 MiB, the
-                                   kernel that also runs routing and down);
+                                   token, and small batches of layers whose
+                                   experts' gates hold at most 16 MiB each,
+                                   the kernel that also runs routing and
+                                   down);
                                    NULL for none */
     void *prof_event_end;       /* optional hipEvent_t recorded just after it */
     int32_t neuron_budget;      /* MOE_TOPK only: active neurons per (token,

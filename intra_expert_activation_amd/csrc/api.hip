@@ -117,19 +117,23 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     }
 
     // one-launch decode path: single-token batches (every expert has one
-    // pair), and batches of up to kFusedMaxT tokens when an expert's gate
-    // matrix is at most 16 MiB.  That path gives each (token, slot) pair its
-    // own workgroups, so an expert chosen by several tokens has its rows read
-    // once per pair, mostly from cache while the pairs run together; with
-    // small experts that costs less than the grouping and the separate down
-    // launch save.  Measured (us per call, grouped -> one launch): Qwen-style
-    // T 2/4/8: 43.6/50.5/67.2 -> 24.0/33.1/52.1; DeepSeek-style with shared
-    // experts: 50.5/62.3/84.8 -> 30.7/44.3/76.4; Mixtral-style (117 MiB gate
-    // per expert) T 2: 122 -> 126, so it keeps the grouped path from T 2.
+    // pair), and small batches of layers whose experts' gate matrices hold at
+    // most 16 MiB: up to 8 tokens, or up to kFusedMaxT when there are no
+    // shared experts and T * K <= E (about one pair per touched expert).  That
+    // path gives each (token, slot) pair its own workgroups, so an expert
+    // chosen by several tokens (a shared expert by all of them) has its rows
+    // read once per pair, mostly from cache while the pairs run together; with
+    // small experts and few repeats that costs less than the grouping and the
+    // separate down launch save.  Measured (us per call, grouped -> one
+    // launch): Qwen-style T 2/4/8/12/16: 43.6/50.5/67.2/78.5/94.0 ->
+    // 24.0/33.1/52.1/69.4/88.6, T 24: 114 -> 126; DeepSeek-style (2 shared
+    // experts) T 2/4/8: 50.5/62.3/84.8 -> 30.7/44.3/76.4, T 12: 98 -> 113;
+    // Mixtral-style (117 MiB of gate per expert) T 2: 122 -> 126.
     {
         const size_t gate_bytes = (size_t)p->Imax * p->H * (p->dtype == MOE_BF16 ? 2 : 4);
-        p->fused = !calib && !p->topk && T >= 1 && (T == 1 || (T <= kFusedMaxT && gate_bytes <= ((size_t)16 << 20)))
-                       ? 1 : 0;
+        const bool small = gate_bytes <= ((size_t)16 << 20) &&
+                           (T <= 8 || (p->S == 0 && T <= kFusedMaxT && T * p->K <= p->E));
+        p->fused = !calib && !p->topk && T >= 1 && (T == 1 || small) ? 1 : 0;
     }
 
     // workspace layout

@@ -18,7 +18,7 @@ constexpr int kMaxRowsPerChunk = 256;
 constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
 constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
 constexpr int kMfmaMinPairs = 16;  // pair-count threshold of the MFMA path
-constexpr int kFusedMaxT = 8;      // most tokens of a batch on the one-launch decode path
+constexpr int kFusedMaxT = 16;     // most tokens of a batch on the one-launch decode path
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a

@@ -326,13 +326,13 @@ def test_single_token_path(cfg, over, q):
     check_layer(L, DL, x[:1], logits[:1], None, mode=moe.MOE_DENSE, tol=tol)
 
 
-@pytest.mark.parametrize("cfg,T,q", [(2, 2, 0.85), (2, 4, 0.85), (2, 8, 0.70), (4, 3, 0.85), (4, 8, 0.85),
-                                     (1, 5, 0.8), (3, 2, 0.9)])
+@pytest.mark.parametrize("cfg,T,q", [(2, 2, 0.85), (2, 4, 0.85), (2, 8, 0.70), (2, 12, 0.85), (2, 16, 0.85),
+                                     (4, 3, 0.85), (4, 8, 0.85), (1, 5, 0.8), (3, 2, 0.9)])
 def test_few_token_batches(cfg, T, q):
-    # up to 8 tokens of small-expert layers take the one-launch path (an
-    # expert chosen by several tokens, and the shared experts, have several
-    # pairs whose masks form its union); the Mixtral-style layer's 2 tokens
-    # take the grouped path
+    # up to 8 tokens of small-expert layers (16 without shared experts and
+    # with T * K <= E) take the one-launch path (an expert chosen by several
+    # tokens, and the shared experts, have several pairs whose masks form its
+    # union); the Mixtral-style layer's 2 tokens take the grouped path
     c, L = cached_layer(cfg, (("I", 4096),) if cfg == 3 else ())  # 32 MiB of gate per expert
     DL = layer_to_device(L)
     x, logits = synth.make_tokens(c, 2, 3 * T)
