@@ -21,7 +21,7 @@
 //               and h = m ? a*u : 0 of those rows stored compacted
 //               [64 tokens][active rows] as a bf16 pair (hi + lo = h to
 //               ~2^-17) so the down product keeps fp32-level accuracy.
-//  k_down_mfma  (item, 128-column tile): O = sum over neuron tiles of
+//  down body   (item, 128-column tile), in the merged down kernel: O = sum over neuron tiles of
 //               H_tile[64 x active] * W_down[active rows, 128 cols]; the
 //               neuron-major down rows are staged row-major in LDS and read
 //               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
@@ -32,9 +32,9 @@
 
 namespace moe {
 
-// Standalone launches, for layers whose GEMV projection workgroups are not
-// 256 threads wide (H below 2048 in bf16): the merged kernels host these
-// bodies otherwise.
+// Standalone launch of the MFMA projection, for layers whose GEMV projection
+// does not fit the merged kernel (rows wider than 2048 bf16, or fewer than 4
+// wavefronts); the down tiles always run in the merged down kernel.
 template <int MODE>
 __global__ __launch_bounds__(256, 3) void k_proj_mfma(MfmaParams p)
 {
@@ -42,12 +42,6 @@ __global__ __launch_bounds__(256, 3) void k_proj_mfma(MfmaParams p)
     mfma_proj_body<MODE>(p, S, blockIdx.x);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void k_down_mfma(MfmaParams p)
-{
-    __shared__ MfmaDownLds S;
-    mfma_down_body<MODE>(p, S, blockIdx.x);
-}
 
 static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
 
@@ -57,15 +51,6 @@ hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipS
     const dim3 grid(round8((long long)pl.max_pairs * pl.NT)), block(256);
     if (mode == MOE_DENSE) hipLaunchKernelGGL(k_proj_mfma<MOE_DENSE>, grid, block, 0, st, mp);
     else hipLaunchKernelGGL(k_proj_mfma<MOE_SPARSE>, grid, block, 0, st, mp);
-    return hipGetLastError();
-}
-
-hipError_t launch_down_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t st)
-{
-    if (!pl.use_mfma) return hipSuccess;
-    const dim3 grid(round8((long long)pl.max_items * (pl.H / kTC))), block(256);
-    if (mode == MOE_DENSE) hipLaunchKernelGGL(k_down_mfma<MOE_DENSE>, grid, block, 0, st, mp);
-    else hipLaunchKernelGGL(k_down_mfma<MOE_SPARSE>, grid, block, 0, st, mp);
     return hipGetLastError();
 }
 

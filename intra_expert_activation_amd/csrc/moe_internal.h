@@ -202,7 +202,6 @@ hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t s
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
 hipError_t launch_topk_select(const Plan &pl, const TopkParams &tp, hipStream_t stream);
 hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
-hipError_t launch_down_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
 // The one-launch decode path and its combine; the events (optional) bracket
 // the first launch.
 hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEvent_t ev_begin, hipEvent_t ev_end,
