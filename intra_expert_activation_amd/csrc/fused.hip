@@ -247,8 +247,10 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 // ---------------------------------------------------------------------------
 // k_fcombine.  Workgroups [0, T * H / 64): y of one token over 64 columns.
 // Its 16 thread groups take the token's partial rows (slot, chunk) in a fixed
-// interleave, each adding w_slot * row (w = 1 for a shared expert), and the
-// group sums meet in LDS in a fixed order, so y is reproducible bit for bit.
+// interleave, each adding w_slot * row (w = 1 for a shared expert), with the
+// loads of 16 rows per thread in flight together (one memory round trip for up
+// to 256 rows), and the group sums meet in LDS in a fixed order, so y is
+// reproducible bit for bit.
 // Workgroups after those (only when a union output is requested): one per
 // expert, OR of its pairs' mask words, then the union size and the ascending
 // list of its active neurons.
@@ -270,11 +272,12 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
         const int R = p.slots * p.C;  // partial rows of the token, (slot, chunk) order
         const float *src = p.partial + (size_t)t * R * p.H + col;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int i0 = g; i0 < R; i0 += 64) {
-            float4 v[4];
-            float wv[4];
+        constexpr int kRows = 16;  // rows per thread whose loads are in flight together
+        for (int i0 = g; i0 < R; i0 += 16 * kRows) {
+            float4 v[kRows];
+            float wv[kRows];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {  // four rows' loads at once (indices clamped, extras unused)
+            for (int j = 0; j < kRows; ++j) {  // indices clamped, extras unused
                 const int i = min(i0 + 16 * j, R - 1);
                 const int slot = i / p.C;
                 v[j] = *reinterpret_cast<const float4 *>(src + (size_t)i * p.H);
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
                 wv[j] = slot < p.K ? ws : 1.f;
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < kRows; ++j)
                 if (i0 + 16 * j < R) {
                     acc.x = fmaf(wv[j], v[j].x, acc.x);
                     acc.y = fmaf(wv[j], v[j].y, acc.y);
