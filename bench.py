@@ -53,7 +53,7 @@ def kernel_src_sha256():
 
 # name: (config id, default batch, default q, default sweep, description)
 WORKLOADS = {
-    "decode": (2, 64, 0.85, "1,8,32", "qwen-moe-style decode layer: H 2048, 128 experts x I 768, top-8"),
+    "decode": (2, 64, 0.85, "1,8,16,32", "qwen-moe-style decode layer: H 2048, 128 experts x I 768, top-8"),
     "prefill": (5, 4096, 0.70, "", "qwen-moe-style prefill layer: H 2048, 128 experts x I 768, top-8"),
     "mixtral": (3, 16, 0.90, "1,128", "mixtral-style layer: H 4096, 8 experts x I 14336, top-2"),
     "deepseek": (4, 64, 0.85, "1,8,32", "deepseek-v2-lite-style layer: H 2048, 64 experts x I 1408 top-6 "
