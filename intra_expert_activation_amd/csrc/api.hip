@@ -131,8 +131,11 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // Mixtral-style (117 MiB of gate per expert) T 2: 122 -> 126.
     {
         const size_t gate_bytes = (size_t)p->Imax * p->H * (p->dtype == MOE_BF16 ? 2 : 4);
+        // (in DENSE mode every row of every pair is streamed, so repeats cost
+        // three times as much: Qwen-style dense T 16 went from 165 to 199 us,
+        // and that mode keeps the limit of 8)
         const bool small = gate_bytes <= ((size_t)16 << 20) &&
-                           (T <= 8 || (p->S == 0 && T <= kFusedMaxT && T * p->K <= p->E));
+                           (T <= 8 || (mode != MOE_DENSE && p->S == 0 && T <= kFusedMaxT && T * p->K <= p->E));
         p->fused = !calib && !p->topk && T >= 1 && (T == 1 || small) ? 1 : 0;
     }
 
