@@ -166,7 +166,7 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_items = take((size_t)p->max_items * 4);
     p->off_pairs = take((size_t)p->max_pairs * 4);
     p->off_blockcnt = take((size_t)((p->A + kGroupBlock - 1) / kGroupBlock) * p->E * 4);
-    p->off_order = take((size_t)p->EX * 4);
+    p->off_order = take((size_t)p->EX * 16);
     p->off_nact = take(blocks * 4);
     p->off_list = take(blocks * 64);
     p->off_hhi = take(blocks * 64 * 64 * 2);

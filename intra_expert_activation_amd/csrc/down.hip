@@ -364,13 +364,15 @@ __device__ __forceinline__ void down_gemv(const DownParams &p, DownLds &D, int g
     for (int r = 0; r < 2; ++r) {
         const int s = 2 * threadIdx.x + r;
         wl[r] = ul[r] = 0;
+        // slot-ordered experts, pair counts, offsets and union sizes: one round
+        // of independent loads, issued with the load of the touched count (the
+        // index is clamped into the arrays; slots past the count are not used)
+        const int sc = min(s, EX - 1);
+        const int xe = p.touched[sc];
+        const int n = p.slot_n[sc];
+        const int of = p.slot_off[sc];
+        const int uc = MODE == MOE_DENSE ? 0 : p.ucount[sc];
         if (s < ntouched) {
-            // slot-ordered experts, pair counts, offsets and union sizes: one
-            // round of independent loads
-            const int xe = p.touched[s];
-            const int n = p.slot_n[s];
-            const int of = p.slot_off[s];
-            const int uc = MODE == MOE_DENSE ? 0 : p.ucount[s];
             const int Iw = xe >= p.E ? p.Is : p.I;
             D.xe[s] = xe;
             D.n[s] = n;

@@ -89,7 +89,8 @@ struct GroupParams {
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
     int32_t *pairs;       // [max_pairs] (first item << 1 | has a second) for the MFMA projection
     int32_t *blockcnt;    // [ceil(A / kGroupBlock), E] per-block expert counts (large batches), or null
-    int32_t *order;       // [EX] (slot << 16 | expert) of the touched experts, by descending pair count
+    int32_t *order;       // [EX][4] (slot << 16 | expert, pairs, first pair, 0) of the touched experts,
+                          // by descending pair count
 };
 
 struct ProjParams {

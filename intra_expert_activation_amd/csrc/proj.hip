@@ -202,17 +202,20 @@ __device__ __forceinline__ void proj_gemv(const ProjParams &p, ProjLds<NW, TTMAX
     using V = typename Tr::V;
     const int r = bid / p.C;  // rank of the expert in the longest-first order
     const int c = bid - r * p.C;
-    if (r >= p.hdr[0]) return;
-    const int ord = p.order[r];
-    const int s = ord >> 16;  // touched slot
-    const int xe = ord & 0xffff;
+    // r < max_touched <= E + S: the entry is in bounds, and it is read together
+    // with the count of touched experts (ranks past it hold stale entries)
+    const int ntouched = p.hdr[0];
+    const int4 ord = reinterpret_cast<const int4 *>(p.order)[r];
+    if (r >= ntouched) return;
+    const int s = ord.x >> 16;  // touched slot
+    const int xe = ord.x & 0xffff;
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
     const int r0 = c * kChunk;
     if (r0 >= Ie) return;
-    const int n = p.counts[xe];
+    const int n = ord.y;
     if (n >= p.nm) return;  // this expert takes the MFMA path
-    const int off = p.offsets[xe];
+    const int off = ord.z;
     constexpr int rowV = NW * NSW * kWave;  // 16-byte vectors per row (H / epl)
     const size_t mat = (size_t)(shared ? xe - p.E : xe) * Ie * rowV;
     const int lane = threadIdx.x & (kWave - 1);

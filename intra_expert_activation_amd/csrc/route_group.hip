@@ -249,7 +249,9 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         // wavefront 0 writes the metadata: a lane's class counts are packed
         // three to an int, 10 bits each (a class holds at most 512 experts,
         // so no field carries into the next), and summed across the lanes by
-        // prefix scans.
+        // prefix scans.  Each entry also carries the expert's pair count and
+        // first grouped pair, so a projection workgroup finds its work with
+        // one load.
         constexpr int kPer = kMaxExperts / kWave;
         constexpr int kCls = 16;
         constexpr int kWords = (kCls + 2) / 3;
@@ -270,6 +272,10 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
             }
         }
         int slot = wave_incl_scan_dpp(ntl) - ntl;  // slot of this lane's first touched expert
+        int lsum = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) lsum += (lane * kPer + i < EX) ? s_tot[lane * kPer + i] : 0;
+        int first = wave_incl_scan_dpp(lsum) - lsum;  // first grouped pair of this lane's first expert
         int pos[kWords];  // next position of each class for this lane, packed
         int run = 0;      // experts in the classes before (uniform)
 #pragma unroll
@@ -293,11 +299,13 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
                 int w = 0;
 #pragma unroll
                 for (int j = 0; j < kWords; ++j) w = (c / 3 == j) ? pos[j] : w;
-                p.order[(w >> sh) & 1023] = (slot << 16) | (lane * kPer + i);
+                const int e = lane * kPer + i;
+                reinterpret_cast<int4 *>(p.order)[(w >> sh) & 1023] = make_int4((slot << 16) | e, s_tot[e], first, 0);
 #pragma unroll
                 for (int j = 0; j < kWords; ++j) pos[j] += (c / 3 == j) ? 1 << sh : 0;
                 ++slot;
             }
+            first += (lane * kPer + i < EX) ? s_tot[lane * kPer + i] : 0;
         }
     }
     __syncthreads();
