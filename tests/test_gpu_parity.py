@@ -252,8 +252,9 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 64), (4, 64), (2, 1), (4, 1), (4, 8)])
-def test_graph_replay_matches_eager(cfg, T):
+@pytest.mark.parametrize("cfg,T,mode", [(2, 64, moe.MOE_SPARSE), (4, 64, moe.MOE_SPARSE), (2, 1, moe.MOE_SPARSE),
+                                        (4, 1, moe.MOE_SPARSE), (4, 8, moe.MOE_SPARSE), (2, 64, moe.MOE_TOPK)])
+def test_graph_replay_matches_eager(cfg, T, mode):
     # the benchmark's launch configuration: calls captured in one HIP graph
     # (one per batch, in order, sharing a workspace) and replayed several times
     # with eager work between the replays; every replay must reproduce the
@@ -268,12 +269,13 @@ def test_graph_replay_matches_eager(cfg, T):
         x, lg = synth.make_tokens(c, 2, (r + 1) * T)
         batches.append((dev_tensor(x[r * T:], DL["dtype"]), torch.from_numpy(np.ascontiguousarray(lg[r * T:])).cuda()))
     shape = moe.layer_shape(batches[0][0], DL["w_gate"], L["K"], bool(L["renormalize"]), shared[0] if shared else None)
-    ws = moe.alloc_workspace(moe.workspace_size(shape), "cuda")
+    ws = moe.alloc_workspace(moe.workspace_size(shape, mode), "cuda")
 
     def call(r, out=None):
         x, lg = batches[r]
         return moe.sparse_expert_ffn(x, lg, DL["w_gate"], DL["w_up"], DL["w_down"], tau, K=L["K"],
-                                     renormalize=bool(L["renormalize"]), shared=shared, out=out, workspace=ws)
+                                     renormalize=bool(L["renormalize"]), shared=shared, out=out, workspace=ws,
+                                     mode=mode, neuron_budget=115)
 
     eager = [{k: v.clone() for k, v in call(r).items()} for r in range(3)]
     outs = [{k: torch.empty_like(v) for k, v in e.items()} for e in eager]
