@@ -418,6 +418,31 @@ def test_topk_variant(cfg, T, frac):
         np.testing.assert_array_equal(g["union_idx"][e, :len(want)], want)
 
 
+def test_topk_variant_edge_cases():
+    c, L = cached_layer(4, (("E", 16), ("I", 256)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 12)
+    W = max(L["I"], L["I_shared"]) // 32
+    # budget 0: nothing active; a budget of every row: the dense layer
+    g0 = gpu_ffn(DL, x, logits, None, mode=moe.MOE_TOPK, neuron_budget=0)
+    assert (g0["y"] == 0).all() and (g0["mask_bits"] == 0).all() and (g0["union_cnt"] == 0).all()
+    gall = gpu_ffn(DL, x, logits, None, mode=moe.MOE_TOPK, neuron_budget=10_000)
+    de = oracle.moe(L, x, logits, 0.0, dense=True)
+    assert rel_l2(gall["y"], de.y) <= TOL_BF16
+    rows = np.where(slot_experts(gall["topk_ids"], L["E"], L["S"]) < L["E"], L["I"], L["I_shared"])
+    assert (unpack_bits(gall["mask_bits"], W * 32).sum(axis=-1) == rows).all()
+    # a NaN hidden state makes every score of that token NaN: NaN ranks first and
+    # equal keys go to the lower rows, so its pairs keep rows 0 .. budget - 1
+    xn = x.copy()
+    xn[4, 7] = 0x7FC0  # bf16 NaN
+    g = gpu_ffn(DL, xn, logits, None, mode=moe.MOE_TOPK, neuron_budget=37)
+    on = unpack_bits(g["mask_bits"][4], W * 32)
+    assert (on[:, :37].all() and not on[:, 37:].any())
+    assert np.isnan(g["y"][4]).all() and np.isfinite(np.delete(g["y"], 4, axis=0)).all()
+    o = oracle.moe_topk(L, xn, logits, 37)
+    np.testing.assert_array_equal(unpack_bits(o.mask_bits[4], W * 32), on)
+
+
 # ---------------------------------------------------------------------------
 # Routing alone
 # ---------------------------------------------------------------------------
