@@ -164,6 +164,31 @@ def test_route_matches_sort_and_softmax(renorm):
     assert (np.diff(w, axis=1) <= 0).all()  # slots in descending weight order
 
 
+@pytest.mark.parametrize("renorm", [0, 1])
+def test_route_nan_and_infinite_logits(renorm):
+    # the routing conventions for non-finite logits (a reading: the router is
+    # unchanged by the method and the pages give no rule): a NaN logit ranks as
+    # -inf; a NaN or +inf logit makes the softmax denominator NaN, so every
+    # weight of that token is NaN; a -inf logit is an ordinary probability 0
+    logits = np.array([[0.5, np.nan, 2.0, -1.0, 0.0],      # NaN: never chosen before finite ones
+                       [np.inf, 1.0, 3.0, 0.0, -2.0],      # +inf ranks first
+                       [-np.inf, 1.0, -np.inf, 0.5, 0.25],  # -inf: weight 0 when chosen
+                       [np.nan, np.nan, 1.0, np.nan, np.nan]], np.float32)  # NaN ties: lower id first
+    ids, w = oracle.route(logits, 3, renorm)
+    np.testing.assert_array_equal(ids, [[2, 0, 4], [0, 2, 1], [1, 3, 4], [2, 0, 1]])
+    assert np.isnan(w[0]).all() and np.isnan(w[1]).all() and np.isnan(w[3]).all()
+    # row 2 is finite: the plain definition with exp(-inf) = 0
+    p = np.exp(logits[2].astype(np.float64) - 1.0)
+    p /= p.sum()
+    sel = p[[1, 3, 4]]
+    if renorm:
+        sel = sel / sel.sum()
+    np.testing.assert_allclose(w[2], sel, rtol=1e-13)
+    ids4, w4 = oracle.route(logits[2:3], 5, renorm)
+    np.testing.assert_array_equal(ids4, [[1, 3, 4, 0, 2]])
+    assert w4[0, 3] == 0 and w4[0, 4] == 0
+
+
 # --------------------------------------------------------------------------
 # Whole-layer definition against the textbook MoE built from library routines
 # --------------------------------------------------------------------------
