@@ -12,11 +12,13 @@
  * --------------------------------
  *  - Every array pointer is a DEVICE pointer owned by the caller (for example
  *    a PyTorch tensor's data_ptr()).  The library never allocates, frees or
- *    retains memory, keeps no global state, and never synchronises the host:
- *    each call only validates its arguments and enqueues kernels on
- *    `hip_stream` (a hipStream_t; NULL means the default stream).  Calls are
- *    therefore capturable in a HIP graph.  Concurrent calls on different
- *    streams need separate workspaces.
+ *    retains caller memory and never synchronises the host: each call only
+ *    validates its arguments and enqueues kernels on `hip_stream` (a
+ *    hipStream_t; NULL means the default stream).  Calls are therefore
+ *    capturable in a HIP graph.  Concurrent calls on different streams need
+ *    separate workspaces.  The only state kept between calls is a per-device
+ *    cache of an occupancy query (how many down-projection workgroups a
+ *    device holds at once), read and written atomically.
  *  - Errors that the host can detect are returned before any HIP call is
  *    made (so they are reported even on a machine without a GPU):
  *      MOE_ERR_INVALID_ARG  a NULL required pointer, a non-positive size,
@@ -54,7 +56,8 @@ typedef enum {
     MOE_ERR_HIP = 4
 } moe_status;
 
-/* Element type of the hidden states and of every weight matrix. */
+/* Element type of the hidden states (x_dtype) and of the weight matrices
+ * (w_dtype). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* MOE_SPARSE applies the threshold mask; MOE_DENSE computes the ordinary
@@ -75,17 +78,19 @@ typedef enum { MOE_SPARSE = 0, MOE_DENSE = 1, MOE_TOPK = 2 } moe_mode;
  *   K  experts per token (top-K routing), 1 <= K <= E, K <= 32
  *   S  shared experts (always active, weight 1; may be 0); I_shared their
  *      intermediate size (ignored when S = 0)
- *   dtype        moe_dtype of x and of all weights
+ *   x_dtype      moe_dtype of the hidden states x
+ *   w_dtype      moe_dtype of every weight matrix (routed and shared)
  *   renormalize  1: the K routing weights are divided by their sum;
  *                0: they are the softmax probabilities over all E experts
  * Supported by the kernels (else MOE_ERR_UNSUPPORTED):
- *   H = s * 64 * L with s in {1,2,4,8,16}, where L = 8 for bf16 and 4 for f32
- *   (so H in {512,1024,2048,4096,8192} for bf16); I and I_shared multiples of
- *   32 and at most 16384; E + S <= 512.
+ *   x_dtype == w_dtype (bf16 weights with bf16 hidden states, or fp32 with
+ *   fp32); H = s * 64 * L with s in {1,2,4,8,16}, where L = 8 for bf16 and 4
+ *   for f32 (so H in {512,1024,2048,4096,8192} for bf16); I and I_shared
+ *   multiples of 32 and at most 16384; E + S <= 512.
  */
 typedef struct {
     int32_t T, H, E, I, K, S, I_shared;
-    int32_t dtype;
+    int32_t x_dtype, w_dtype;
     int32_t renormalize;
 } moe_shape;
 
@@ -110,9 +115,9 @@ moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t K,
 /* Arguments of moe_sparse_expert_ffn.  Shapes refer to moe_shape; W denotes
  * ceil(max(I, I_shared)/32) and Imax = max(I, I_shared). */
 typedef struct {
-    const void *x;              /* [T,H] dtype, 16-byte aligned */
+    const void *x;              /* [T,H] x_dtype, 16-byte aligned */
     const float *router_logits; /* [T,E] fp32 */
-    const void *w_gate;         /* [E,I,H] dtype, neuron-major, 16-byte aligned */
+    const void *w_gate;         /* [E,I,H] w_dtype, neuron-major, 16-byte aligned */
     const void *w_up;           /* [E,I,H] */
     const void *w_down;         /* [E,I,H] neuron-major (transpose of [H,I]) */
     const void *ws_gate;        /* [S,I_shared,H] or NULL when S = 0 */
@@ -138,15 +143,6 @@ typedef struct {
     float *topk_w;              /* OUT or NULL: [T,K] as moe_route_topk */
     void *workspace;            /* device scratch, 256-byte aligned */
     size_t workspace_bytes;     /* >= moe_workspace_size(shape, mode) */
-    void *prof_event_begin;     /* optional hipEvent_t recorded on the stream
-                                   just before the expert projection kernel
-                                   (gate/score/mask/up; for batches of one
-                                   token, and small batches of layers whose
-                                   experts' gates hold at most 16 MiB each,
-                                   the kernel that also runs routing and
-                                   down);
-                                   NULL for none */
-    void *prof_event_end;       /* optional hipEvent_t recorded just after it */
     int32_t neuron_budget;      /* MOE_TOPK only: active neurons per (token,
                                    slot) pair, >= 0; an expert with fewer rows
                                    keeps all of them.  The order is |a_j|
@@ -157,7 +153,8 @@ typedef struct {
 /*
  * Workspace bytes that moe_sparse_expert_ffn needs for this shape and mode
  * (depends on the shape only, never on the data).  Returns MOE_OK and sets
- * *bytes, or an error for an invalid / unsupported shape.
+ * *bytes, or the status that moe_sparse_expert_ffn would return for an
+ * invalid / unsupported shape (so a caller learns which check failed).
  */
 moe_status moe_workspace_size(const moe_shape *shape, int32_t mode, size_t *bytes);
 
@@ -202,7 +199,7 @@ moe_status moe_calibrate_workspace_size(const moe_shape *shape, int32_t Tc, size
  * population's value.  floor(q*N) is evaluated in double precision on the
  * float q.  NaN scores order after +infinity.  With no ties among the scores,
  * exactly floor(q*N) of them are < tau.
- *   x_calib [Tc,H] dtype; logits_calib [Tc,E] fp32; w_gate / ws_gate as in
+ *   x_calib [Tc,H] x_dtype; logits_calib [Tc,E] fp32; w_gate / ws_gate as in
  *   moe_ffn_args; tau_out [E+S] fp32.  Tc >= 1; q in [0,1].
  */
 moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib,
@@ -213,13 +210,6 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib,
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *moe_status_string(int32_t status);
-
-/* Timing helpers for benchmarks: a hipEvent_t with timing enabled, destroyed
- * by moe_timer_destroy; moe_timer_elapsed_ms waits for `end` and returns the
- * milliseconds between two recorded events. */
-moe_status moe_timer_create(void **event);
-moe_status moe_timer_destroy(void *event);
-moe_status moe_timer_elapsed_ms(void *begin, void *end, float *ms);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "moe_internal.h"
+#include "moe_sparse_prof.h"
 
 namespace moe {
 
@@ -24,9 +25,12 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     if (T < 0 || s->H <= 0 || s->E <= 0 || s->I <= 0 || s->K <= 0 || s->K > s->E || s->S < 0)
         return MOE_ERR_INVALID_ARG;
     if (s->S > 0 && s->I_shared <= 0) return MOE_ERR_INVALID_ARG;
-    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->x_dtype != MOE_F32 && s->x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (s->renormalize != 0 && s->renormalize != 1) return MOE_ERR_INVALID_ARG;
     if (s->K > kMaxK) return MOE_ERR_UNSUPPORTED;
+    // the kernels take hidden states and weights of one element type
+    if (s->x_dtype != s->w_dtype) return MOE_ERR_UNSUPPORTED;
 
     memset(p, 0, sizeof *p);
     p->T = T;
@@ -36,9 +40,9 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->K = s->K;
     p->S = s->S;
     p->Is = s->S > 0 ? s->I_shared : 0;
-    p->dtype = s->dtype;
+    p->dtype = s->w_dtype;
     p->renorm = s->renormalize;
-    p->epl = s->dtype == MOE_BF16 ? 8 : 4;
+    p->epl = s->w_dtype == MOE_BF16 ? 8 : 4;
     if (p->H % (kWave * p->epl) != 0) return MOE_ERR_UNSUPPORTED;
     p->NS = p->H / (kWave * p->epl);
     if (p->NS != 1 && p->NS != 2 && p->NS != 4 && p->NS != 8 && p->NS != 16) return MOE_ERR_UNSUPPORTED;
@@ -233,8 +237,13 @@ moe_status moe_route_topk(const float *logits, int32_t T, int32_t E, int32_t K, 
                : MOE_ERR_HIP;
 }
 
-moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe_ffn_args *a,
-                                 void *hip_stream)
+}  // extern "C"
+
+namespace moe {
+
+// The layer call; ev_begin / ev_end (optional) bracket the projection kernel.
+static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_args *a, hipEvent_t ev_begin,
+                          hipEvent_t ev_end, void *hip_stream)
 {
     if (!shape || !a) return MOE_ERR_INVALID_ARG;
     Plan pl;
@@ -286,7 +295,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
         fp.y = a->y;
         fp.T = pl.T; fp.H = pl.H; fp.E = pl.E; fp.I = pl.I; fp.Is = pl.Is; fp.S = pl.S; fp.K = pl.K;
         fp.slots = pl.slots; fp.P = pl.P; fp.C = pl.C; fp.W = pl.W; fp.Imax = pl.Imax; fp.renorm = pl.renorm;
-        return launch_fused(pl, fp, mode, (hipEvent_t)a->prof_event_begin, (hipEvent_t)a->prof_event_end, stream)
+        return launch_fused(pl, fp, mode, ev_begin, ev_end, stream)
                        == hipSuccess
                    ? MOE_OK
                    : MOE_ERR_HIP;
@@ -334,8 +343,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     mp.slots = pl.slots; mp.NT = pl.NT; mp.max_items = pl.max_items;
 
     // the events bracket the expert projection (gate, score, mask, up) of both paths
-    if (a->prof_event_begin && hipEventRecord((hipEvent_t)a->prof_event_begin, stream) != hipSuccess)
-        return MOE_ERR_HIP;
+    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return MOE_ERR_HIP;
     if (pl.topk) {
         // every pair's gate scores, the per-pair selection of the budget
         // largest, then the projection under those masks (up and h; the gate
@@ -351,8 +359,7 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     } else if (launch_proj(pl, pp, mp, mode, stream) != hipSuccess) {
         return MOE_ERR_HIP;
     }
-    if (a->prof_event_end && hipEventRecord((hipEvent_t)a->prof_event_end, stream) != hipSuccess)
-        return MOE_ERR_HIP;
+    if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return MOE_ERR_HIP;
 
     DownParams dp{};
     dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
@@ -371,6 +378,21 @@ moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe
     cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe_ffn_args *args, void *hip_stream)
+{
+    return ffn_call(shape, mode, args, nullptr, nullptr, hip_stream);
+}
+
+moe_status moe_sparse_expert_ffn_profiled(const moe_shape *shape, int32_t mode, const moe_ffn_args *args,
+                                          void *ev_begin, void *ev_end, void *hip_stream)
+{
+    return ffn_call(shape, mode, args, (hipEvent_t)ev_begin, (hipEvent_t)ev_end, hip_stream);
 }
 
 moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, const float *logits_calib,

@@ -23,6 +23,7 @@
 // slot): piece k of pair (t, slot) is row t * slots + slot of partial slice
 // k, and the last piece of a group stores the group's piece count for the
 // combine.
+#include <atomic>
 #include <type_traits>
 
 #include "mfma_body.h"
@@ -538,20 +539,25 @@ __global__ __launch_bounds__(256, 3) void k_down_bf16(DownParams p, MfmaParams m
 
 static int round8_down(long long v) { return (int)((v + 7) / 8 * 8); }
 
-// Workgroups of `kernel` (256 threads) the current device holds at once, per
-// kernel and device (queried once).
-template <class Kernel>
-static int resident_blocks(Kernel kernel)
+// Workgroups of kernel KF (256 threads) the current device holds at once.
+// The query is cached per kernel and device; calls from several host threads
+// may race to fill an entry, which is harmless because every thread computes
+// the same value and the entry is read and written atomically.
+template <auto KF>
+static int resident_blocks()
 {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KF, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     const int r = per_cu * cus;
-    if (dev < 64) cache[dev] = r;
+    if (dev < 64) cache[dev].store(r, std::memory_order_relaxed);
     return r;
 }
 
@@ -570,13 +576,13 @@ static hipError_t launch_down_m(const Plan &pl, const DownParams &dp_in, const M
     DownParams dp = dp_in;
     if constexpr (std::is_same<Tr, BF16>::value) {
         if (pl.use_mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
-            dp.GD = down_groups(pl, resident_blocks(k_down_bf16<MODE>));
+            dp.GD = down_groups(pl, resident_blocks<k_down_bf16<MODE>>());
             const int grid = dp.GD + round8_down((long long)pl.max_items * (pl.H / kTC));
             hipLaunchKernelGGL((k_down_bf16<MODE>), dim3(grid), dim3(256), 0, st, dp, mp);
             return hipGetLastError();
         }
     }
-    dp.GD = down_groups(pl, resident_blocks(k_down<Tr, MODE>));
+    dp.GD = down_groups(pl, resident_blocks<k_down<Tr, MODE>>());
     hipLaunchKernelGGL((k_down<Tr, MODE>), dim3(dp.GD), dim3(256), 0, st, dp);
     return hipGetLastError();
 }

@@ -1,12 +1,15 @@
 """The C ABI without a GPU: the library loads, exports every symbol that
-include/moe_sparse.h declares, and rejects invalid calls before any HIP call
-(so these run on a CPU-only host).  Pointers used here are never dereferenced:
-every call below fails validation first."""
+include/*.h declares, and rejects invalid calls before any HIP call (so these
+run on a CPU-only host).  Pointers used here are never dereferenced: every
+call below fails validation first.  The binding's own argument checks, which
+guard what the C ABI cannot see (sizes, element types, devices), run on CPU
+tensors and raise before any library call."""
 import ctypes
 import os
 import re
 
 import pytest
+import torch
 
 from intra_expert_activation_amd import moe
 
@@ -21,17 +24,25 @@ def L():
     return moe.lib()
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "moe_sparse.h")).read()
+def _declared(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
     return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*\**\s*(moe_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol(L):
-    names = _declared()
-    assert len(names) == 9, names
-    assert set(names) == set(moe.EXPORTS)
-    for n in names:
+    names = _declared("moe_sparse.h")
+    assert set(names) == set(moe.EXPORTS), names
+    prof = _declared("moe_sparse_prof.h")
+    assert set(prof) == set(moe.PROF_EXPORTS), prof
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["moe_sparse.h", "moe_sparse_prof.h"], headers
+    for n in names + prof:
         assert hasattr(L, n), n
+
+
+def test_product_header_has_no_measurement_hooks():
+    text = open(os.path.join(ROOT, "include", "moe_sparse.h")).read()
+    assert "timer" not in text and "event" not in text
 
 
 def test_status_strings(L):
@@ -73,6 +84,9 @@ def test_workspace_size_valid_and_shape_only(L):
     (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(H=0), moe.MOE_ERR_INVALID_ARG),
     (dict(dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(x_dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(x_dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),      # fp32 x with bf16 weights
+    (dict(dtype=moe.MOE_F32, x_dtype=moe.MOE_BF16, H=1024), moe.MOE_ERR_UNSUPPORTED),
     (dict(renormalize=2), moe.MOE_ERR_INVALID_ARG),
     (dict(S=1, I_shared=0), moe.MOE_ERR_INVALID_ARG),
     (dict(H=2000), moe.MOE_ERR_UNSUPPORTED),         # not 64 lanes x 16 bytes
@@ -196,6 +210,96 @@ def test_timer_validation(L):
     assert moe.lib().moe_timer_create(None) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_timer_destroy(None) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_timer_elapsed_ms(None, None, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_profiled_call_validates_like_the_plain_one(L):
+    f = moe.lib().moe_sparse_expert_ffn_profiled
+    assert f(ctypes.byref(_shape()), 0, ctypes.byref(_args(x=None)), None, None, None) == moe.MOE_ERR_INVALID_ARG
+    a = _args()
+    a.workspace_bytes = 16
+    assert f(ctypes.byref(_shape()), 0, ctypes.byref(a), None, None, None) == moe.MOE_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------------------------
+# The binding's argument checks (CPU tensors: every rejection happens before
+# the device check, and a well-formed call fails only there)
+# ---------------------------------------------------------------------------
+def _layer_tensors(T=4, H=512, E=6, I=64, S=0, Is=64, dt=torch.bfloat16):
+    t = dict(x=torch.zeros(T, H, dtype=dt), router_logits=torch.zeros(T, E),
+             w_gate=torch.zeros(E, I, H, dtype=dt), w_up=torch.zeros(E, I, H, dtype=dt),
+             w_down=torch.zeros(E, I, H, dtype=dt), tau=torch.zeros(E + S))
+    if S:
+        t["shared"] = tuple(torch.zeros(S, Is, H, dtype=dt) for _ in range(3))
+    return t
+
+
+def _call(t, **kw):
+    t = dict(t)
+    x, lg, wg, wu, wd, tau = (t.pop(k) for k in ("x", "router_logits", "w_gate", "w_up", "w_down", "tau"))
+    args = dict(K=2)
+    args.update(t)
+    args.update(kw)
+    return moe.sparse_expert_ffn(x, lg, wg, wu, wd, tau, **args)
+
+
+def test_binding_accepts_a_well_formed_call_up_to_the_device():
+    with pytest.raises(ValueError, match="GPU"):
+        _call(_layer_tensors())
+    with pytest.raises(ValueError, match="GPU"):
+        _call(_layer_tensors(S=2))
+
+
+@pytest.mark.parametrize("change,exc", [
+    (dict(x=torch.zeros(4, 512, dtype=torch.float16)), TypeError),            # unsupported dtype
+    (dict(x=torch.zeros(4, 512)), TypeError),                                 # fp32 x, bf16 weights
+    (dict(router_logits=torch.zeros(4, 6, dtype=torch.bfloat16)), TypeError), # logits not fp32
+    (dict(router_logits=torch.zeros(5, 6)), ValueError),                      # wrong T
+    (dict(w_up=torch.zeros(6, 64, 512)), TypeError),                          # fp32 up, bf16 gate
+    (dict(w_down=torch.zeros(6, 512, 64, dtype=torch.bfloat16)), ValueError), # [E,H,I], not neuron-major
+    (dict(w_gate=torch.zeros(6, 64, 256, dtype=torch.bfloat16)), ValueError), # rows of the wrong width
+    (dict(tau=torch.zeros(5)), ValueError),                                   # shorter than E + S
+    (dict(tau=torch.zeros(6, dtype=torch.float64)), TypeError),
+    (dict(x=torch.zeros(512, 4, dtype=torch.bfloat16).t()), ValueError),      # not contiguous
+])
+def test_binding_rejects(change, exc):
+    t = _layer_tensors()
+    t.update(change)
+    with pytest.raises(exc):
+        _call(t)
+
+
+def test_binding_rejects_bad_shared_and_outputs():
+    t = _layer_tensors(S=2)
+    g, u, d = t["shared"]
+    t["shared"] = (g, u, torch.zeros(2, 64, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        _call(t)
+    t = _layer_tensors(S=2)
+    t["tau"] = torch.zeros(6)  # E + S = 8 thresholds are needed
+    with pytest.raises(ValueError):
+        _call(t)
+    with pytest.raises(ValueError):
+        _call(_layer_tensors(), out=dict(y=torch.zeros(4, 256)))
+    with pytest.raises(TypeError):
+        _call(_layer_tensors(), out=dict(mask_bits=torch.zeros(4, 2, 2)))
+    with pytest.raises(ValueError):
+        _call(_layer_tensors(), out=dict(union_cnt=torch.zeros(5, dtype=torch.int32)))
+    t = _layer_tensors()
+    t["tau"] = None
+    with pytest.raises(ValueError, match="tau is required"):
+        _call(t)
+
+
+def test_binding_rejects_calibration_arguments():
+    t = _layer_tensors()
+    with pytest.raises(TypeError):
+        moe.calibrate_threshold(t["x"], t["router_logits"].to(torch.bfloat16), t["w_gate"], 0.5, K=2)
+    with pytest.raises(TypeError):
+        moe.calibrate_threshold(t["x"].float(), t["router_logits"], t["w_gate"], 0.5, K=2)
+    with pytest.raises(ValueError):
+        moe.calibrate_threshold(t["x"], t["router_logits"], t["w_gate"], 0.5, K=2, tau_out=torch.zeros(3))
+    with pytest.raises(ValueError, match="GPU"):
+        moe.calibrate_threshold(t["x"], t["router_logits"], t["w_gate"], 0.5, K=2)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
