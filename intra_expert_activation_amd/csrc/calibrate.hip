@@ -42,7 +42,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectParams p)
     float result;
     const double kappa_d = floor((double)p.q * (double)N);
     if (N == 0) {
-        result = __builtin_nanf("");  // no population: the caller falls back
+        result = 0.f;  // no population (unused: the finalize step falls back by the pair count)
     } else if (p.q == 0.f) {
         result = 0.f;
     } else if (kappa_d >= (double)N) {
@@ -85,17 +85,19 @@ __global__ __launch_bounds__(1024) void k_select(SelectParams p)
 }
 
 // tau_out[e]: routed experts take the routed population's value (or their own
-// when per_expert, falling back to the routed value without pairs); shared
-// experts take the shared population's value (or their own).
-__global__ void k_select_finalize(const float *taus, int E, int S, int per_expert, float *tau_out)
+// when per_expert, falling back to the routed value when the expert has no
+// calibration pair); shared experts take the shared population's value (or
+// their own; a shared expert has a pair for every token).  An expert's own
+// order statistic is kept even when it is NaN (NaN scores order after
+// +infinity, so a high q over a population holding NaN scores selects one):
+// only the pair count, never the value, decides the fallback.
+__global__ void k_select_finalize(const float *taus, const int32_t *counts, int E, int S, int per_expert,
+                                  float *tau_out)
 {
     const int e = blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= E + S) return;
     float t = (e < E) ? taus[0] : taus[1];
-    if (per_expert) {
-        const float own = taus[2 + e];
-        if (!isnan(own)) t = own;
-    }
+    if (per_expert && counts[e] > 0) t = taus[2 + e];
     tau_out[e] = t;
 }
 
@@ -105,7 +107,7 @@ hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out,
     hipLaunchKernelGGL(k_select, dim3(pops), dim3(1024), 0, st, sp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_select_finalize, dim3((sp.EX + 255) / 256), dim3(256), 0, st, sp.taus,
+    hipLaunchKernelGGL(k_select_finalize, dim3((sp.EX + 255) / 256), dim3(256), 0, st, sp.taus, sp.counts,
                        sp.E, sp.S, sp.per_expert, tau_out);
     return hipGetLastError();
 }

@@ -92,7 +92,8 @@ def test_qwen_decode_dense():
 # DeepSeek-V2-Lite-style layer: 64 routed (top-6, no renormalisation) + 2
 # shared experts on the sparse path, Zipf-skewed routing
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T,q", [(1, 0.85), (8, 0.85), (32, 0.85), (64, 0.85), (64, 0.70)])
+@pytest.mark.parametrize("T,q", [(1, 0.85), (8, 0.85), (32, 0.85), (64, 0.85), (1, 0.70), (8, 0.70), (32, 0.70),
+                                 (64, 0.70)])
 def test_deepseek_shared(T, q):
     c, L = cached_layer(4)
     DL = layer_to_device(L)
@@ -118,6 +119,26 @@ def test_deepseek_block_grouping(T):
     print(f"T={T} err={s['err']:.2e} band={s['band']} flips={s['flips']}")
 
 
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_deepseek_shared_kept_dense(T):
+    # the policy of keeping the shared experts dense (their neurons matter
+    # more): tau_shared = 0 with the routed experts at their calibrated tau.
+    # Every shared-slot mask bit is set, the routed slots stay sparse, and y
+    # matches the oracle.  T 1 and 8 take the one-launch path, 40 the grouped
+    # path with the shared experts on the MFMA body.
+    c, L = cached_layer(4)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, 0.85, calib_tokens=16).copy()
+    tau[L["E"]:] = 0.0
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+    m = unpack_bits(s["gpu"]["mask_bits"], max(L["I"], L["I_shared"]))
+    K = L["K"]
+    assert m[:, K:, :L["I_shared"]].all()
+    assert m[:, :K, :L["I"]].mean() < 0.3
+    assert (s["gpu"]["union_cnt"][L["E"]:] == L["I_shared"]).all()
+
+
 def test_deepseek_per_expert_tau():
     c, L = cached_layer(4)
     DL = layer_to_device(L)
@@ -140,22 +161,24 @@ def test_mixtral_reduced_ragged(T, q):
     check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
 
 
-@pytest.mark.parametrize("T", [1, 16, 128])
-def test_mixtral_full_sampled(T):
+@pytest.mark.parametrize("T,q", [(1, 0.9), (16, 0.9), (128, 0.9), (256, 0.9), (16, 0.7), (128, 0.7)])
+def test_mixtral_full_sampled(T, q):
+    # full I = 14336: T 128 and 256 put every expert on the MFMA path
     c, L = cached_layer(3)
     DL = layer_to_device(L)
     x, logits = synth.make_tokens(c, 2, T)
-    tau = _tau(L, c, 0.9, calib_tokens=8)
+    tau = _tau(L, c, q, calib_tokens=8)
     rows = np.unique(np.r_[0, T - 1, T // 2])
     s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16, rows_idx=rows)
-    print(f"T={T} err={s['err']:.2e}")
+    print(f"T={T} q={q} err={s['err']:.2e}")
 
 
 # ---------------------------------------------------------------------------
 # Qwen-MoE-style prefill (4096 tokens): every output row the oracle checks is
 # sampled; unions are checked against the GPU's own masks at full size
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("q,mode", [(0.5, moe.MOE_SPARSE), (0.9, moe.MOE_SPARSE), (None, moe.MOE_DENSE)])
+@pytest.mark.parametrize("q,mode", [(0.5, moe.MOE_SPARSE), (0.7, moe.MOE_SPARSE), (0.9, moe.MOE_SPARSE),
+                                    (None, moe.MOE_DENSE)])
 def test_qwen_prefill_sampled(q, mode):
     # every expert has ~256 pairs here: the MFMA path
     c, L = cached_layer(5)
@@ -503,20 +526,55 @@ def test_calibrate(cfg, q, per_expert):
     if q in (0.0, 1.0):
         return
     # realised sparsity: the FFN's masks on the calibration tokens leave
-    # floor(q*N) scores below tau, up to the scores that fp32 rounding of a
-    # different summation order (GEMV vs MFMA path) can move across tau: those
-    # within 1e-5*tau of it
+    # floor(q*N) scores of each population below its tau, up to the scores that
+    # fp32 rounding of a different summation order (GEMV vs MFMA path) can move
+    # across tau: those within 1e-5*tau of it.  With per_expert every expert
+    # with calibration pairs is its own population.
     g = gpu_ffn(DL, xc, lc, tau_g.astype(np.float32))
-    if per_expert:
-        return
     o = oracle.moe(L, xc, lc, np.inf, want_scores=True)
     m = unpack_bits(g["mask_bits"], max(L["I"], L["I_shared"]))
-    groups = [(slice(0, L["K"]), L["I"], tau_g[0])]
-    if L["S"]:
-        groups.append((slice(L["K"], L["K"] + L["S"]), L["I_shared"], tau_g[-1]))
-    for sl, rows, t in groups:
-        inactive = int((~m[:, sl, :rows]).sum())
-        v = np.abs(o.scores[:, sl, :rows]).ravel()
+    K, S, E = L["K"], L["S"], L["E"]
+    exp = slot_experts(o.ids, E, S)
+    pops = []  # (selector over [t, slot], rows, tau)
+    if per_expert:
+        for e in range(E + S):
+            sel = exp == e
+            if sel.any():
+                pops.append((sel, L["I"] if e < E else L["I_shared"], tau_g[e]))
+    else:
+        pops.append((exp < E, L["I"], tau_g[0]))
+        if S:
+            pops.append((exp >= E, L["I_shared"], tau_g[-1]))
+    for sel, rows, t in pops:
+        inactive = int((~m[sel][:, :rows]).sum())
+        v = np.abs(o.scores[sel][:, :rows]).ravel()
         kappa = int(np.floor(float(np.float32(q)) * v.size))
         slack = int((np.abs(v - t) <= 1e-5 * t).sum())
         assert kappa - slack <= inactive <= kappa + slack, (inactive, kappa, slack)
+
+
+@pytest.mark.parametrize("per_expert", [False, True])
+def test_calibrate_nan_scores(per_expert):
+    # a NaN hidden state makes every score of its token NaN; NaN orders after
+    # +inf, so a high q selects NaN for the populations it reaches, and an
+    # expert's own NaN order statistic is kept (only an expert with no
+    # calibration pair falls back to the routed value)
+    c, L = cached_layer(1)
+    DL = layer_to_device(L)
+    xc, lc = synth.make_tokens(c, 1)
+    xc = xc.copy()
+    xc[5, 3] = np.nan
+    for q in (0.8, 0.97, 0.99):
+        tau_g = moe.calibrate_threshold(dev_tensor(xc, L["dtype"]), torch.from_numpy(lc).cuda(), DL["w_gate"], q,
+                                        K=L["K"], per_expert=per_expert).cpu().numpy().astype(np.float64)
+        tau_o = oracle.calibrate(L, xc, lc, q, per_expert=per_expert)
+        np.testing.assert_array_equal(np.isnan(tau_g), np.isnan(tau_o))
+        fin = np.isfinite(tau_o)
+        np.testing.assert_allclose(tau_g[fin], tau_o[fin], rtol=1e-4, atol=2e-6)
+        if q == 0.97:
+            # the routed population's value is finite; with per_expert the NaN
+            # token's own experts select NaN (the old sentinel would have
+            # replaced it by the routed value)
+            assert np.isfinite(tau_o).all() if not per_expert else (np.isnan(tau_o).any() and np.isfinite(tau_o).any())
+        if q == 0.99:
+            assert np.isnan(tau_o).any()  # the case is exercised

@@ -395,6 +395,49 @@ def test_calibration_monotone_and_per_expert():
             assert per[e] == np.partition(v, kappa)[kappa]
 
 
+def _scalar_gate_layer(E, I):
+    """H = 1 and every gate weight 1, so every neuron of a token scores
+    |SiLU(x_t)|: the calibration population is known by hand."""
+    ones = np.ones((E, I, 1), np.float32)
+    return dict(H=1, E=E, I=I, K=1, S=0, I_shared=0, renormalize=1, dtype="f32",
+                w_gate=ones, w_up=ones.copy(), w_down=ones.copy())
+
+
+def _silu(g):
+    return g / (1.0 + math.exp(-g))
+
+
+def test_calibration_orders_nan_after_infinity():
+    # tokens x = 1, +inf, NaN, -2 to the one expert, 4 neurons each: the
+    # ascending population is |SiLU(-2)| x4, SiLU(1) x4, +inf x4 (SiLU(+inf) =
+    # +inf), NaN x4, so with N = 16 the order statistic v[floor(16 q)] is
+    L = _scalar_gate_layer(E=1, I=4)
+    x = np.array([[1.0], [np.inf], [np.nan], [-2.0]], np.float32)
+    logits = np.zeros((4, 1), np.float32)
+    want = {0.25: _silu(1.0), 0.5: np.inf, 0.6875: np.inf, 0.75: np.nan, 0.9375: np.nan, 0.125: -_silu(-2.0)}
+    for q, t in want.items():
+        got = oracle.calibrate(L, x, logits, q)[0]
+        if np.isnan(t):
+            assert np.isnan(got), (q, got)
+        else:
+            assert got == pytest.approx(t, rel=1e-15), (q, got, t)
+
+
+def test_calibration_per_expert_nan_is_kept_and_no_pairs_fall_back():
+    # expert 1 takes only the NaN token, expert 2 takes none, expert 0 the rest
+    L = _scalar_gate_layer(E=3, I=4)
+    x = np.array([[np.nan], [1.0], [-2.0], [3.0]], np.float32)
+    logits = np.array([[0, 5, -9], [5, 0, -9], [5, 0, -9], [5, 0, -9]], np.float32)
+    tau = oracle.calibrate(L, x, logits, 0.5, per_expert=True)
+    # expert 0: |SiLU(-2)| x4, SiLU(1) x4, SiLU(3) x4 -> v[6] = SiLU(1)
+    assert tau[0] == pytest.approx(_silu(1.0), rel=1e-15)
+    # expert 1: its own population is NaN x4 -> NaN, kept (it has pairs)
+    assert np.isnan(tau[1])
+    # expert 2: no pair -> the routed population's value: 12 finite, 4 NaN -> v[8] = SiLU(3)
+    assert tau[2] == pytest.approx(_silu(3.0), rel=1e-15)
+    assert oracle.calibrate(L, x, logits, 0.5)[0] == tau[2]
+
+
 # --------------------------------------------------------------------------
 # The top-k alternative to the threshold ([TS] Methodology, Activation
 # Masking contrasts the two): per-pair selection of the budget largest |a|
