@@ -16,9 +16,11 @@
  *    validates its arguments and enqueues kernels on `hip_stream` (a
  *    hipStream_t; NULL means the default stream).  Calls are therefore
  *    capturable in a HIP graph.  Concurrent calls on different streams need
- *    separate workspaces.  The only state kept between calls is a per-device
+ *    separate workspaces.  The state kept between calls is a per-device
  *    cache of an occupancy query (how many down-projection workgroups a
- *    device holds at once), read and written atomically.
+ *    device holds at once), read and written atomically, and, for
+ *    moe_sparse_expert_ffn_noalloc only, its fixed scratch array per device
+ *    and that array's device address.
  *  - Errors that the host can detect are returned before any HIP call is
  *    made (so they are reported even on a machine without a GPU):
  *      MOE_ERR_INVALID_ARG  a NULL required pointer, a non-positive size,
@@ -180,6 +182,26 @@ moe_status moe_workspace_size(const moe_shape *shape, int32_t mode, size_t *byte
  */
 moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode,
                                  const moe_ffn_args *args, void *hip_stream);
+
+/*
+ * moe_sparse_expert_ffn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  args->workspace and
+ * args->workspace_bytes are ignored: the call uses a fixed scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, and it calls no allocating routine.  Shapes whose
+ * moe_workspace_size(shape, mode) exceeds that size return
+ * MOE_ERR_WORKSPACE before any HIP call (64 MiB holds the decode layers of
+ * the workloads above up to 64 tokens; a prefill batch needs a workspace).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (the kernels clear what must start at zero): calls that overlap
+ * on one GPU (on different streams, or from several host threads) race and
+ * must be serialised by the caller.  Outputs, errors and determinism are
+ * those of moe_sparse_expert_ffn.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_sparse_expert_ffn_noalloc(const moe_shape *shape, int32_t mode,
+                                         const moe_ffn_args *args, void *hip_stream);
 
 /*
  * Workspace bytes for moe_calibrate_threshold with Tc calibration tokens.

@@ -9,6 +9,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 #include "moe_sparse_prof.h"
 
@@ -387,6 +390,66 @@ extern "C" {
 moe_status moe_sparse_expert_ffn(const moe_shape *shape, int32_t mode, const moe_ffn_args *args, void *hip_stream)
 {
     return ffn_call(shape, mode, args, nullptr, nullptr, hip_stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+// Scratch of moe_sparse_expert_ffn_noalloc: a fixed device array, one per GPU
+// the library runs on, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: the device address comes
+// from hipGetSymbolAddress, once per device, and only that address is passed
+// to the kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void *> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's scratch address (looked up on the first call on that
+// device, with that device current), or null with *err set.
+static void *scratch_address(moe_status *err)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = MOE_ERR_HIP;
+        return nullptr;
+    }
+    void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            *err = MOE_ERR_HIP;
+            return nullptr;
+        }
+        g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_sparse_expert_ffn_noalloc(const moe_shape *shape, int32_t mode, const moe_ffn_args *args,
+                                         void *hip_stream)
+{
+    if (!shape || !args) return MOE_ERR_INVALID_ARG;
+    Plan pl;
+    const moe_status st = make_plan(shape, mode, 0, &pl);
+    if (st != MOE_OK) return st;
+    if (pl.T == 0) return MOE_OK;
+    if (pl.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;  // before any HIP call
+    moe_status err = MOE_OK;
+    void *ptr = scratch_address(&err);
+    if (!ptr) return err;
+    moe_ffn_args a = *args;
+    a.workspace = ptr;
+    a.workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+    return ffn_call(shape, mode, &a, nullptr, nullptr, hip_stream);
 }
 
 moe_status moe_sparse_expert_ffn_profiled(const moe_shape *shape, int32_t mode, const moe_ffn_args *args,

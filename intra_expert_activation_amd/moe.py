@@ -21,9 +21,11 @@ MOE_SPARSE, MOE_DENSE, MOE_TOPK = 0, 1, 2
 
 # every symbol include/moe_sparse.h declares
 EXPORTS = (
-    "moe_route_topk", "moe_workspace_size", "moe_sparse_expert_ffn",
+    "moe_route_topk", "moe_workspace_size", "moe_sparse_expert_ffn", "moe_sparse_expert_ffn_noalloc",
     "moe_calibrate_workspace_size", "moe_calibrate_threshold", "moe_status_string",
 )
+# bytes of the fixed scratch array moe_sparse_expert_ffn_noalloc uses
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # every symbol include/moe_sparse_prof.h declares (measurement hooks)
 PROF_EXPORTS = (
     "moe_sparse_expert_ffn_profiled", "moe_timer_create", "moe_timer_destroy", "moe_timer_elapsed_ms",
@@ -67,6 +69,7 @@ def lib():
         L.moe_workspace_size.argtypes = [sp, i32, ctypes.POINTER(sz)]
         L.moe_sparse_expert_ffn.argtypes = [sp, i32, ctypes.POINTER(MoeFfnArgs), vp]
         L.moe_sparse_expert_ffn_profiled.argtypes = [sp, i32, ctypes.POINTER(MoeFfnArgs), vp, vp, vp]
+        L.moe_sparse_expert_ffn_noalloc.argtypes = [sp, i32, ctypes.POINTER(MoeFfnArgs), vp]
         L.moe_calibrate_workspace_size.argtypes = [sp, i32, ctypes.POINTER(sz)]
         L.moe_calibrate_threshold.argtypes = [sp, vp, vp, i32, vp, vp, ctypes.c_float, i32, vp, vp, sz, vp]
         L.moe_status_string.argtypes = [i32]
@@ -186,7 +189,7 @@ def route_topk(logits: torch.Tensor, K: int, renormalize: bool = True):
 
 def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, renormalize=True,
                       shared=None, mode=MOE_SPARSE, want_masks=True, out=None, workspace=None,
-                      prof_events=None, neuron_budget=0):
+                      prof_events=None, neuron_budget=0, noalloc=False):
     """One MoE layer forward.  ``shared`` = (ws_gate, ws_up, ws_down) or None.
 
     ``mode`` MOE_TOPK keeps the ``neuron_budget`` largest |SiLU(gate)| neurons
@@ -195,7 +198,10 @@ def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, re
     [T,K+S,W] int32 (bit patterns), ``union_idx`` [E+S,Imax], ``union_cnt`` [E+S],
     ``topk_ids`` and ``topk_w``.  ``out`` may supply preallocated outputs.
     ``prof_events`` (a pair of library timers' handles) brackets the expert
-    projection kernel through moe_sparse_expert_ffn_profiled.
+    projection kernel through moe_sparse_expert_ffn_profiled.  ``noalloc``
+    calls moe_sparse_expert_ffn_noalloc, which takes no workspace (the
+    library's fixed per-device scratch instead; calls on one GPU must not
+    overlap).
     Raises TypeError / ValueError for a tensor of the wrong dtype, shape,
     layout or device before anything is launched.
     """
@@ -246,9 +252,12 @@ def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, re
         for k, (shp, dt) in shapes.items():
             if k not in o:
                 o[k] = torch.empty(shp, dtype=dt, device=dev)
-    need = workspace_size(shape, mode)
-    if workspace is None or workspace.numel() < need:
-        workspace = alloc_workspace(need, dev)
+    if noalloc:
+        _need(workspace is None and prof_events is None, "noalloc takes no workspace and no events")
+    else:
+        need = workspace_size(shape, mode)
+        if workspace is None or workspace.numel() < need:
+            workspace = alloc_workspace(need, dev)
     a = MoeFfnArgs()
     a.x, a.router_logits = _ptr(x), _ptr(router_logits)
     a.w_gate, a.w_up, a.w_down = _ptr(w_gate), _ptr(w_up), _ptr(w_down)
@@ -257,9 +266,12 @@ def sparse_expert_ffn(x, router_logits, w_gate, w_up, w_down, tau=None, *, K, re
     a.y = _ptr(o["y"])
     a.mask_bits, a.union_idx, a.union_cnt = (_ptr(o.get(k)) for k in ("mask_bits", "union_idx", "union_cnt"))
     a.topk_ids, a.topk_w = _ptr(o.get("topk_ids")), _ptr(o.get("topk_w"))
-    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    a.workspace, a.workspace_bytes = (_ptr(workspace), workspace.numel()) if workspace is not None else (None, 0)
     a.neuron_budget = int(neuron_budget)
-    if prof_events is not None:
+    if noalloc:
+        _check(lib().moe_sparse_expert_ffn_noalloc(ctypes.byref(shape), int(mode), ctypes.byref(a), _stream(dev)),
+               "moe_sparse_expert_ffn_noalloc")
+    elif prof_events is not None:
         _check(lib().moe_sparse_expert_ffn_profiled(ctypes.byref(shape), int(mode), ctypes.byref(a),
                                                     prof_events[0], prof_events[1], _stream(dev)),
                "moe_sparse_expert_ffn_profiled")
