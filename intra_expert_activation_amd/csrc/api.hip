@@ -122,6 +122,12 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
         // an expert with k tiles has ceil(k / 2) pairs
         p->max_pairs = (p->max_items + big + p->S + 1) / 2;
     }
+    // pairs of the GEMV experts (fewer than nm pairs each when the MFMA path
+    // is on): the rows of the down pieces after the first
+    {
+        const long long g = p->use_mfma ? (long long)p->EX * (p->nm - 1) : (long long)p->P;
+        p->G = (int)(g < p->P ? g : p->P);
+    }
 
     // one-launch decode path: single-token batches (every expert has one
     // pair), and small batches of layers whose experts' gate matrices hold at
@@ -167,7 +173,13 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_ucount = take((size_t)p->EX * 4);
     p->off_npc = take(calib ? 0 : (size_t)p->P * p->NCT * 4);
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
-    p->off_partial = take(calib ? 0 : (size_t)(p->fused ? p->C : p->KMAX) * p->P * p->H * 4);
+    // down outputs: piece 0 of every pair [P, H]; the later pieces only for
+    // the GEMV experts' pairs [KMAX - 1, G, H] (the one-launch path keeps its
+    // chunk partial rows [P, C, H] here instead)
+    p->off_partial = take(calib ? 0
+                                : (p->fused ? (size_t)p->C * p->P : (size_t)p->P + (size_t)(p->KMAX - 1) * p->G) *
+                                      p->H * 4);
+    p->off_cidx = take(calib ? 0 : (size_t)p->P * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
     const size_t blocks = (size_t)p->max_items * p->NT;
     p->off_items = take((size_t)p->max_items * 4);
@@ -316,6 +328,7 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
     gp.nm = pl.nm;
     gp.items = ws_at<int32_t>(ws, pl.off_items);
     gp.pairs = ws_at<int32_t>(ws, pl.off_pairs);
+    gp.cidx = ws_at<int32_t>(ws, pl.off_cidx);
     gp.blockcnt = ws_at<int32_t>(ws, pl.off_blockcnt);
     gp.order = ws_at<int32_t>(ws, pl.off_order);
     if (launch_route_group(a->router_logits, pl.renorm, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;
@@ -368,6 +381,7 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
     dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
     dp.hdr = hdr; dp.counts = counts; dp.offsets = offsets; dp.touched = touched; dp.slot_n = slot_n; dp.slot_off = slot_off;
     dp.union_words = union_words; dp.ucount = ucount; dp.partial = partial; dp.npc = npc;
+    dp.cidx = gp.cidx; dp.G = pl.G;
     dp.pair_tok = pair_tok; dp.pair_slot = pair_slot; dp.slots = pl.slots;
     dp.union_idx = a->union_idx; dp.union_cnt = a->union_cnt;
     dp.H = pl.H; dp.E = pl.E; dp.I = pl.I; dp.Is = pl.Is; dp.S = pl.S; dp.A = pl.A; dp.P = pl.P;
@@ -377,8 +391,8 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
     if (launch_down(pl, dp, mp, pl.topk ? MOE_SPARSE : mode, stream) != hipSuccess) return MOE_ERR_HIP;
 
     CombineParams cp{};
-    cp.partial = partial; cp.topk_w = w; cp.npc = npc; cp.y = a->y;
-    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT;
+    cp.partial = partial; cp.cidx = gp.cidx; cp.topk_w = w; cp.npc = npc; cp.y = a->y;
+    cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT; cp.G = pl.G;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -497,6 +511,7 @@ moe_status moe_calibrate_threshold(const moe_shape *shape, const void *x_calib, 
     gp.hdr = hdr; gp.counts = counts; gp.offsets = offsets; gp.touched = touched; gp.slot_n = slot_n; gp.slot_off = slot_off;
     gp.pair_tok = pair_tok; gp.pair_slot = pair_slot; gp.union_cnt = nullptr;
     gp.union_words = nullptr; gp.W = pl.W; gp.nm = pl.nm; gp.items = nullptr; gp.pairs = nullptr;
+    gp.cidx = nullptr;
     gp.blockcnt = ws_at<int32_t>(workspace, pl.off_blockcnt);
     gp.order = ws_at<int32_t>(workspace, pl.off_order);
     if (launch_route_group(logits_calib, 1, ids, w, gp, stream) != hipSuccess) return MOE_ERR_HIP;

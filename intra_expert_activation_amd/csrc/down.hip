@@ -315,11 +315,13 @@ __device__ __forceinline__ void down_piece(const DownParams &p, const uint16_t *
         for (int c = 0; c < EPL; ++c) acc[t][c] = 0.f;
     down_stream<Tr, TB, MODE>(Wd, rowV, hb, n, t0, nt, list, a, b - a, acc, lane);
 
-    float *dst = p.partial + (size_t)k * p.P * p.H + (size_t)(v0 + lane) * EPL;
+    // piece 0 at the pair's (token, slot) row, later pieces at its compact row
+    const int prow = k == 0 ? orow : p.P + (k - 1) * p.G + p.cidx[orow];
+    float *dst = p.partial + (size_t)(v0 + lane) * EPL;
 #pragma unroll
     for (int t = 0; t < TB; ++t)
         if (t < nt) {
-            const int r = __builtin_amdgcn_readlane(orow, t);
+            const int r = __builtin_amdgcn_readlane(prow, t);
 #pragma unroll
             for (int c = 0; c < EPL; c += 4)
                 *reinterpret_cast<float4 *>(dst + (size_t)r * p.H + c) =
@@ -604,7 +606,8 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 // ---------------------------------------------------------------------------
 // k_combine: y[t] = sum_{k<K} w[t,k] * o[t,k] + sum_{s<S} o[t,K+s].
 // o of a GEMV expert's pair is the sum, in piece order, of the partial sums of
-// the pieces its group (token tile, column tile) was cut into (npc of them);
+// the pieces its group (token tile, column tile) was cut into (npc of them:
+// piece 0 at the pair's (token, slot) row, the others at its compact row);
 // an MFMA expert writes piece 0 only.  A workgroup covers one token and one 256-column tile:
 // 64 column quads x 4 thread groups; group g adds the slots k with k % 4 == g,
 // and the 4 group sums meet in LDS in a fixed order (so the result is
@@ -641,8 +644,10 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
             if (k0 + 4 * j >= p.slots) break;
             const int orow = t * p.slots + k0 + 4 * j;
             float4 v = np[j] > 0 ? o[j] : make_float4(0.f, 0.f, 0.f, 0.f);  // no piece: o = 0
+            const int crow = np[j] > 1 ? p.cidx[orow] : 0;
             for (int kk = 1; kk < np[j]; ++kk) {
-                const float4 w = reinterpret_cast<const float4 *>(p.partial + ((size_t)kk * p.P + orow) * p.H)[c4];
+                const float4 w =
+                    reinterpret_cast<const float4 *>(p.partial + ((size_t)p.P + (size_t)(kk - 1) * p.G + crow) * p.H)[c4];
                 v.x += w.x;
                 v.y += w.y;
                 v.z += w.z;

@@ -50,6 +50,7 @@ struct Plan {
     int NT;          // 64-neuron tiles per expert: ceil(Imax / 64)
     int max_items;   // upper bound on (expert, 64-token tile) work items
     int max_pairs;   // upper bound on pairs of them (the MFMA projection's items)
+    int G;           // upper bound on the pairs of GEMV experts (rows of the down pieces after the first)
     // one-launch decode path (small batches): every (pair, 32-row chunk)
     // runs routing, gate, mask, up and down; a second launch combines
     int fused;
@@ -57,7 +58,7 @@ struct Plan {
     // workspace layout (byte offsets)
     size_t off_ids, off_w, off_hdr, off_counts, off_offsets, off_touched, off_slotn, off_slotoff;
     size_t off_pair_tok, off_pair_slot, off_union, off_ucount, off_npc, off_h, off_partial;
-    size_t off_taus;
+    size_t off_cidx, off_taus;
     size_t off_items, off_pairs, off_blockcnt, off_order, off_nact, off_list, off_hhi, off_hlo;
     size_t off_mw;
     size_t total;
@@ -88,6 +89,8 @@ struct GroupParams {
     int nm;               // MFMA pair-count threshold
     int32_t *items;       // [max_items] (expert << 16 | token tile) of MFMA experts
     int32_t *pairs;       // [max_pairs] (first item << 1 | has a second) for the MFMA projection
+    int32_t *cidx;        // [P] by (t * slots + slot): the pair's row in the down pieces after the
+                          // first (pairs of GEMV experts, numbered in grouped order), -1 for MFMA pairs
     int32_t *blockcnt;    // [ceil(A / kGroupBlock), E] per-block expert counts (large batches), or null
     int32_t *order;       // [EX][4] (slot << 16 | expert, pairs, first pair, 0) of the touched experts,
                           // by descending pair count
@@ -117,23 +120,26 @@ struct DownParams {
     const uint32_t *union_words;
     const int32_t *ucount;  // by touched slot
     const int32_t *pair_tok, *pair_slot;
-    // down output of pair (t, slot): piece k of its 1024-column tile c is
-    // partial[k][t * slots + slot][c * 1024 ...], npc[(t * slots + slot) * NCT + c]
-    // pieces (0: no active row, the output is zero)
-    float *partial;       // [KMAX, P, H]
+    // down output of pair (t, slot): piece 0 of its 1024-column tile c is
+    // row t * slots + slot of partial, piece k >= 1 (GEMV experts only) is
+    // row P + (k - 1) * G + cidx[t * slots + slot]; npc[(t * slots + slot) *
+    // NCT + c] pieces (0: no active row, the output is zero)
+    float *partial;       // [P + (KMAX - 1) * G, H]
+    const int32_t *cidx;  // [P]
     int32_t *npc;         // [P, NCT]
     int32_t *union_idx;   // optional output [EX, Imax]
     int32_t *union_cnt;   // optional output [EX]
-    int H, E, I, Is, S, A, P, W, Imax, NCT, KMAX, GD, slots;
+    int H, E, I, Is, S, A, P, W, Imax, NCT, KMAX, GD, G, slots;
     int nm;
 };
 
 struct CombineParams {
     const float *partial; // as DownParams
+    const int32_t *cidx;  // as DownParams
     const float *topk_w;
     const int32_t *npc;   // as DownParams
     float *y;
-    int T, H, K, slots, P, NCT;
+    int T, H, K, slots, P, NCT, G;
 };
 
 struct MfmaParams {

@@ -89,6 +89,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_before[kMaxExperts];  // this expert's pairs in earlier blocks
     __shared__ int s_tot[kMaxExperts];     // pairs per expert (the whole batch)
+    __shared__ int s_mb[kMaxExperts];      // pairs of MFMA experts before this expert (grouped order)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wv = tid / kWave;
@@ -167,6 +168,18 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         const int incl = wave_incl_scan_dpp(sum);
         int run = incl - sum;
         int ntouched_before = 0;
+        // pairs of the MFMA experts before each expert: a GEMV expert's pairs
+        // take the compact rows [offset - that, ...) of the down pieces
+        int msum = 0;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) msum += (lane * kPer + i < EX && loc[i] >= p.nm) ? loc[i] : 0;
+        int mrun = wave_incl_scan_dpp(msum) - msum;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int e = lane * kPer + i;
+            if (e < EX) s_mb[e] = mrun;
+            mrun += (e < EX && loc[i] >= p.nm) ? loc[i] : 0;
+        }
         // touched list needs the counts in ascending expert order
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
@@ -343,6 +356,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
                 const int t = a / p.K, k = a - t * p.K;
                 p.pair_tok[pos] = t;
                 p.pair_slot[pos] = k;
+                if (p.cidx) p.cidx[t * p.slots + k] = (s_off[e + 1] - s_off[e] >= p.nm) ? -1 : pos - s_mb[e];
             }
         }
     }
@@ -353,6 +367,7 @@ __device__ __forceinline__ void group_body(const GroupParams &p, const int32_t *
         const int pos = p.A + i;
         p.pair_tok[pos] = t;
         p.pair_slot[pos] = p.K + s;
+        if (p.cidx) p.cidx[t * p.slots + p.K + s] = (p.T >= p.nm) ? -1 : pos - s_mb[p.E + s];
     }
 }
 

@@ -100,6 +100,25 @@ def test_workspace_size_rejects(L, kw, code):
     assert _ws(_shape(**kw))[0] == code
 
 
+def test_workspace_bounded_at_prefill_size(L):
+    # the down projection's pieces after the first exist only for pairs of
+    # experts below the MFMA pair threshold (at most 15 pairs each), so at
+    # 4096 tokens the workspace stays near the [P, H] fp32 outputs instead of
+    # growing with KMAX * P * H (8 pieces: 2.1 GiB)
+    T, H, E, I, K = 4096, 2048, 128, 768, 8
+    P = T * K
+    rc, n = _ws(_shape(T=T, H=H, E=E, I=I, K=K))
+    assert rc == moe.MOE_OK
+    outputs = P * H * 4                        # piece 0 of every pair
+    gemv_pieces = 7 * min(P, E * 15) * H * 4    # pieces 1..7 of the GEMV experts' pairs
+    h = P * I * 4                              # h of the GEMV path (the routed pairs' rows)
+    max_items = P // 64 + min(P // 16, E)
+    mfma_tiles = max_items * (I // 64) * 64 * 64 * 2 * 2   # compacted h per (item, 64-row tile), hi and lo
+    assert n < outputs + gemv_pieces + h + mfma_tiles + (16 << 20), n
+    assert n < 620 * 2 ** 20, n
+    assert n < 8 * P * H * 4 * 0.3
+
+
 def test_invalid_mode(L):
     assert _ws(_shape(), 5)[0] == moe.MOE_ERR_INVALID_ARG
 
