@@ -50,7 +50,7 @@ def gpu_ffn(DL: dict, x: np.ndarray, logits: np.ndarray, tau, mode=moe.MOE_SPARS
     ld = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).cuda()
     taud = None
     if tau is not None:
-        taud = torch.from_numpy(np.ascontiguousarray(
+        taud = torch.from_numpy(np.array(
             np.broadcast_to(np.asarray(tau, np.float32), (DL["E"] + DL["S"],)))).cuda()
     shared = (DL["ws_gate"], DL["ws_up"], DL["ws_down"]) if DL["S"] else None
     out = moe.sparse_expert_ffn(xd, ld, DL["w_gate"], DL["w_up"], DL["w_down"], taud, K=DL["K"],
