@@ -275,6 +275,26 @@ def test_deterministic():
         assert np.array_equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("T", [1, 64])
+def test_profiled_call_matches_plain(T):
+    # the measurement entry point (events around the dominant kernel) computes
+    # the same outputs bit for bit, and its events bracket a positive time
+    c, L = cached_layer(2)
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, T)
+    tau = _tau(L, c, 0.85, calib_tokens=16)
+    a = gpu_ffn(DL, x, logits, tau)
+    timer = moe.Timer()
+    try:
+        b = gpu_ffn(DL, x, logits, tau, prof_events=timer.events)
+        ms = timer.elapsed_ms()
+    finally:
+        timer.close()
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert 0.0 < ms < 1000.0
+
+
 @pytest.mark.parametrize("cfg,T,mode", [(2, 64, moe.MOE_SPARSE), (4, 64, moe.MOE_SPARSE), (2, 1, moe.MOE_SPARSE),
                                         (4, 1, moe.MOE_SPARSE), (4, 8, moe.MOE_SPARSE), (2, 64, moe.MOE_TOPK)])
 def test_graph_replay_matches_eager(cfg, T, mode):
