@@ -6,8 +6,10 @@
 // and only the active neurons' up and down rows are fetched (Fused Up-Down).
 // Here the whole chain runs inside one workgroup per (pair, 32-row chunk),
 // with no grouping and no h round trip through memory:
-//   route  wavefront 0 routes the pair's token (every workgroup of a token
-//          computes the same top-K; the hidden states load meanwhile);
+//   route  every wavefront selects the pair's token's top K itself (each
+//          workgroup of a token finds the same ids; the hidden states load
+//          meanwhile), so the first gate rows wait on no barrier; the
+//          weights are stored by one extra workgroup per token;
 //   gate   the chunk's 32 gate rows, SiLU, threshold, mask word;
 //   up     the active rows only -> h = a * u, kept in LDS;
 //   down   the active rows' down weights, h-weighted, summed in registers
@@ -34,7 +36,7 @@ struct FusedLds {
     float part[NW][kChunk][1];  // per-wavefront partial dots (gate, then up)
     float a[kChunk];            // scores
     float h[kChunk];            // h of the active rows, by rank
-    int e;                      // the pair's expert
+    uint64_t sel[NW][kSelWords];  // each wavefront's top-K selection words
     uint32_t act;               // active rows of the chunk
 };
 
@@ -74,6 +76,19 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
     constexpr int rowV = NW * NSW * kWave;  // 16-byte vectors per row
     __shared__ FusedLds<NW> L;
 
+    if ((int)blockIdx.x >= p.P * p.C) {  // the routing outputs of one token
+        const int tt = blockIdx.x - p.P * p.C;
+        if (threadIdx.x < kWave) {
+            int id;
+            float wt;
+            route_token(p.logits, tt, p.E, p.K, p.renorm, L.sel[0], id, wt);
+            if ((int)threadIdx.x < p.K) {
+                p.ids[(size_t)tt * p.K + threadIdx.x] = id;
+                p.w[(size_t)tt * p.K + threadIdx.x] = wt;
+            }
+        }
+        return;
+    }
     const int pair = blockIdx.x / p.C;
     const int c = blockIdx.x - pair * p.C;
     const int t = pair / p.slots;
@@ -87,22 +102,8 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 #pragma unroll
     for (int k = 0; k < NSW; ++k) xr[0][k] = reinterpret_cast<const V *>(p.x)[(size_t)t * rowV + vbase + k * kWave];
 
-    if (slot < p.K) {
-        if (wave == 0) {
-            int id;
-            float wt;
-            route_token(p.logits, t, p.E, p.K, p.renorm, id, wt);
-            if (lane == slot) L.e = id;
-            if (slot == 0 && c == 0 && lane < p.K) {  // one workgroup per token stores the routing
-                p.ids[(size_t)t * p.K + lane] = id;
-                p.w[(size_t)t * p.K + lane] = wt;
-            }
-        }
-    } else if (threadIdx.x == 0) {
-        L.e = p.E + slot - p.K;  // shared expert
-    }
-    __syncthreads();
-    const int xe = __builtin_amdgcn_readfirstlane(L.e);
+    int xe = p.E + slot - p.K;  // a shared expert, or else the routed one:
+    if (slot < p.K) xe = __builtin_amdgcn_readlane(route_token_ids(p.logits, t, p.E, p.K, L.sel[wave]), slot);
     const bool shared = xe >= p.E;
     const int Ie = shared ? p.Is : p.I;
     const int r0 = c * kChunk;
@@ -359,7 +360,7 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
 template <class Tr, int NW, int NSW>
 static hipError_t launch_fused_ns(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
 {
-    const dim3 grid((unsigned)(pl.P * pl.C));
+    const dim3 grid((unsigned)(pl.P * pl.C + pl.T));  // + one routing-store workgroup per token
     if (mode == MOE_DENSE)
         hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_DENSE>), grid, dim3(NW * kWave), 0, st, fp);
     else

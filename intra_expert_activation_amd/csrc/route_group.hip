@@ -12,17 +12,19 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // k_route: one wavefront per token.  Each lane holds up to 8 logits (E <= 512).
-// K rounds of a wavefront arg-max pick the experts in descending logit order
-// (ties to the lower id); softmax weights are exp(l - max) / sum exp(l - max).
+// The experts are picked in descending logit order (ties to the lower id) by
+// a ballot search for the K-th largest logit; softmax weights are
+// exp(l - max) / sum exp(l - max).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_route(const float *__restrict__ logits, int T, int E, int K,
                                                int renorm, int32_t *__restrict__ ids, float *__restrict__ w)
 {
+    __shared__ uint64_t s_sel[4][kSelWords];
     const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
     if (t >= T) return;
     int id;
     float wt;
-    route_token(logits, t, E, K, renorm, id, wt);
+    route_token(logits, t, E, K, renorm, s_sel[threadIdx.x / kWave], id, wt);
     const int lane = threadIdx.x & (kWave - 1);
     if (lane < K) {
         ids[(size_t)t * K + lane] = id;
