@@ -202,7 +202,7 @@ __device__ __forceinline__ void down_issue(DownBatch<Tr, TB, UR> &bt, const type
 #pragma unroll
     for (int u = 0; u < UR; ++u) {
         const int j = __builtin_amdgcn_readlane(jw, u);
-        bt.w[u] = Wd[(size_t)j * rowV + lane];
+        bt.w[u] = load_stream(Wd + (size_t)j * rowV + lane);  // read once per call: nontemporal
     }
 }
 

@@ -62,7 +62,9 @@ __device__ __forceinline__ void down_batch(const typename Tr::V (&buf)[UR][NSW],
     }
 }
 
-template <class Tr, int NW, int NSW, int MODE>
+// NT: nontemporal weight loads, for single-token batches (every expert then
+// serves one pair, so no other workgroup reads its rows).
+template <class Tr, int NW, int NSW, int MODE, bool NT>
 __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 {
     using V = typename Tr::V;
@@ -126,21 +128,21 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 
         // ---- gate: 32 rows, two batches in flight, last two peeled -----------
         V bufA[UR][NSW], bufB[UR][NSW];
-        load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);
+        load_rows<Tr, UR, NSW, NT>(bufA, Wg, 0, rowV);
         {
             int b = 0;
 #pragma unroll 1
             for (; b + 2 < NB; b += 2) {
-                load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+                load_rows<Tr, UR, NSW, NT>(bufB, Wg, (b + 1) * UR, rowV);
                 __builtin_amdgcn_sched_barrier(0);
                 reduce_batch<Tr, UR, NSW, 1, NW>(bufA, xr, L.part, wave, b * UR, lane, kidx, owner);
                 __builtin_amdgcn_sched_barrier(0);
-                load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+                load_rows<Tr, UR, NSW, NT>(bufA, Wg, (b + 2) * UR, rowV);
                 __builtin_amdgcn_sched_barrier(0);
                 reduce_batch<Tr, UR, NSW, 1, NW>(bufB, xr, L.part, wave, (b + 1) * UR, lane, kidx, owner);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+            load_rows<Tr, UR, NSW, NT>(bufB, Wg, (b + 1) * UR, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, 1, NW>(bufA, xr, L.part, wave, b * UR, lane, kidx, owner);
             reduce_batch<Tr, UR, NSW, 1, NW>(bufB, xr, L.part, wave, (b + 1) * UR, lane, kidx, owner);
@@ -171,21 +173,21 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
             // ---- up: the active rows, ascending -------------------------------
             {
                 uint32_t rest = act;
-                load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+                load_active_rows<Tr, UR, NSW, NT>(bufA, Wu, rest, last, rowV);
                 int b = 0;
 #pragma unroll 1
                 for (; b + 2 < nb; b += 2) {
-                    load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+                    load_active_rows<Tr, UR, NSW, NT>(bufB, Wu, rest, last, rowV);
                     __builtin_amdgcn_sched_barrier(0);
                     reduce_batch<Tr, UR, NSW, 1, NW>(bufA, xr, L.part, wave, b * UR, lane, kidx, owner);
                     __builtin_amdgcn_sched_barrier(0);
-                    load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+                    load_active_rows<Tr, UR, NSW, NT>(bufA, Wu, rest, last, rowV);
                     __builtin_amdgcn_sched_barrier(0);
                     reduce_batch<Tr, UR, NSW, 1, NW>(bufB, xr, L.part, wave, (b + 1) * UR, lane, kidx, owner);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if (b + 1 < nb) {
-                    load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+                    load_active_rows<Tr, UR, NSW, NT>(bufB, Wu, rest, last, rowV);
                     __builtin_amdgcn_sched_barrier(0);
                     reduce_batch<Tr, UR, NSW, 1, NW>(bufA, xr, L.part, wave, b * UR, lane, kidx, owner);
                     reduce_batch<Tr, UR, NSW, 1, NW>(bufB, xr, L.part, wave, (b + 1) * UR, lane, kidx, owner);
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
             }
             // the first down rows do not depend on h: issue them before the barrier
             uint32_t rest = act;
-            load_active_rows<Tr, UR, NSW>(bufA, Wd, rest, last, rowV);
+            load_active_rows<Tr, UR, NSW, NT>(bufA, Wd, rest, last, rowV);
             __syncthreads();
             if (wave == 0 && lane < kChunk && ((act >> lane) & 1u)) {
                 const int rank = __popc(act & ((1u << lane) - 1u));
@@ -210,17 +212,17 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
             int b = 0;
 #pragma unroll 1
             for (; b + 2 < nb; b += 2) {
-                load_active_rows<Tr, UR, NSW>(bufB, Wd, rest, last, rowV);
+                load_active_rows<Tr, UR, NSW, NT>(bufB, Wd, rest, last, rowV);
                 __builtin_amdgcn_sched_barrier(0);
                 down_batch<Tr, UR, NSW>(bufA, L.h, b * UR, nact, acc);
                 __builtin_amdgcn_sched_barrier(0);
-                load_active_rows<Tr, UR, NSW>(bufA, Wd, rest, last, rowV);
+                load_active_rows<Tr, UR, NSW, NT>(bufA, Wd, rest, last, rowV);
                 __builtin_amdgcn_sched_barrier(0);
                 down_batch<Tr, UR, NSW>(bufB, L.h, (b + 1) * UR, nact, acc);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (b + 1 < nb) {
-                load_active_rows<Tr, UR, NSW>(bufB, Wd, rest, last, rowV);
+                load_active_rows<Tr, UR, NSW, NT>(bufB, Wd, rest, last, rowV);
                 __builtin_amdgcn_sched_barrier(0);
                 down_batch<Tr, UR, NSW>(bufA, L.h, b * UR, nact, acc);
                 down_batch<Tr, UR, NSW>(bufB, L.h, (b + 1) * UR, nact, acc);
@@ -357,15 +359,22 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
 }
 
 // ---------------------------------------------------------------------------
-template <class Tr, int NW, int NSW>
-static hipError_t launch_fused_ns(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
+template <class Tr, int NW, int NSW, bool NT>
+static hipError_t launch_fused_nt(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
 {
     const dim3 grid((unsigned)(pl.P * pl.C + pl.T));  // + one routing-store workgroup per token
     if (mode == MOE_DENSE)
-        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_DENSE>), grid, dim3(NW * kWave), 0, st, fp);
+        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_DENSE, NT>), grid, dim3(NW * kWave), 0, st, fp);
     else
-        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_SPARSE>), grid, dim3(NW * kWave), 0, st, fp);
+        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_SPARSE, NT>), grid, dim3(NW * kWave), 0, st, fp);
     return hipGetLastError();
+}
+
+template <class Tr, int NW, int NSW>
+static hipError_t launch_fused_ns(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
+{
+    return pl.T == 1 ? launch_fused_nt<Tr, NW, NSW, true>(pl, fp, mode, st)
+                     : launch_fused_nt<Tr, NW, NSW, false>(pl, fp, mode, st);
 }
 
 template <class Tr>

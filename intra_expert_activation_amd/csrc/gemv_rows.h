@@ -12,23 +12,29 @@ namespace moe {
 constexpr int kChunk = 32;  // rows per workgroup = bits per mask word
 
 // Issue the loads of UR consecutive rows starting at row r (this lane's NSW
-// vectors of each).
-template <class Tr, int UR, int NSW>
+// vectors of each).  NT: nontemporal loads, for rows that no other workgroup of
+// the call reads (ordinary loads leave them in the caches for workgroups of
+// other pairs of the same expert).
+template <class Tr, int UR, int NSW, bool NT = false>
 __device__ __forceinline__ void load_rows(typename Tr::V (&buf)[UR][NSW], const typename Tr::V *W, int r,
                                           int rowV)
 {
 #pragma unroll
     for (int u = 0; u < UR; ++u)
 #pragma unroll
-        for (int k = 0; k < NSW; ++k) buf[u][k] = W[(size_t)(r + u) * rowV + k * kWave];
+        for (int k = 0; k < NSW; ++k) {
+            const typename Tr::V *q = W + (size_t)(r + u) * rowV + k * kWave;
+            buf[u][k] = NT ? load_stream(q) : *q;
+        }
 }
 
 // Issue the loads of the next UR rows whose bits are set in `rest` (ascending),
 // clearing those bits.  Past the last active row the loads repeat row `last`
 // (the highest active row): every load is unconditional, since a load under a
 // branch makes the compiler wait for all loads in flight where the paths
-// join.  The extra rows' dot products land in slots that are never read.
-template <class Tr, int UR, int NSW>
+// join.  The extra rows' dot products land in slots that are never read.  NT as
+// for load_rows.
+template <class Tr, int UR, int NSW, bool NT = false>
 __device__ __forceinline__ void load_active_rows(typename Tr::V (&buf)[UR][NSW], const typename Tr::V *W,
                                                  uint32_t &rest, int last, int rowV)
 {
@@ -37,7 +43,10 @@ __device__ __forceinline__ void load_active_rows(typename Tr::V (&buf)[UR][NSW],
         const int r = rest ? __ffs(rest) - 1 : last;
         rest &= rest - 1;
 #pragma unroll
-        for (int k = 0; k < NSW; ++k) buf[u][k] = W[(size_t)r * rowV + k * kWave];
+        for (int k = 0; k < NSW; ++k) {
+            const typename Tr::V *q = W + (size_t)r * rowV + k * kWave;
+            buf[u][k] = NT ? load_stream(q) : *q;
+        }
     }
 }
 

@@ -221,6 +221,29 @@ hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEven
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 weights/activations: 8 elements per 16-byte vector.
+// Loads of weight rows that a call streams once: nontemporal, so the caches do
+// not keep them.  Whole 4 KiB rows read this way measured 6.8-7.0 TB/s on
+// MI355X against 6.0-6.1 TB/s with ordinary loads (1 GiB, 512 to 4096
+// workgroups of 256 threads).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4 *p)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2 *p)
+{
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ float4 load_stream(const float4 *p)
+{
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 struct BF16 {
     using V = uint4;
     static constexpr int kEpl = 8;

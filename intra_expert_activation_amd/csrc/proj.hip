@@ -34,6 +34,12 @@
 
 namespace moe {
 
+// Gate and up rows with nontemporal loads: each row is read by one workgroup.
+// An expert's second token tile re-reads them, but keeping the weight stream
+// out of the caches measured faster overall (the rest of the call finds its
+// data there).
+constexpr bool kProjStream = true;
+
 // LDS of one workgroup, sized for the largest token tile.
 template <int NW, int TTMAX>
 struct ProjLds {
@@ -73,7 +79,7 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
     // arithmetic.
     V bufA[UR][NSW], bufB[UR][NSW];
     if constexpr (MODE != kModeMasked)
-        load_rows<Tr, UR, NSW>(bufA, Wg, 0, rowV);  // weights first: they do not wait for the tokens
+        load_rows<Tr, UR, NSW, kProjStream>(bufA, Wg, 0, rowV);  // weights first: they do not wait for the tokens
 
     // this wavefront's slice of the tile's hidden states
     V xr[TT][NSW];
@@ -91,16 +97,16 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
         int b = 0;
 #pragma unroll 1
         for (; b + 2 < NB; b += 2) {
-            load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+            load_rows<Tr, UR, NSW, kProjStream>(bufB, Wg, (b + 1) * UR, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
             __builtin_amdgcn_sched_barrier(0);
-            load_rows<Tr, UR, NSW>(bufA, Wg, (b + 2) * UR, rowV);
+            load_rows<Tr, UR, NSW, kProjStream>(bufA, Wg, (b + 2) * UR, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
             __builtin_amdgcn_sched_barrier(0);
         }
-        load_rows<Tr, UR, NSW>(bufB, Wg, (b + 1) * UR, rowV);
+        load_rows<Tr, UR, NSW, kProjStream>(bufB, Wg, (b + 1) * UR, rowV);
         __builtin_amdgcn_sched_barrier(0);
         reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
         reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
@@ -145,21 +151,21 @@ __device__ __forceinline__ uint32_t proj_tile(const ProjParams &p, ProjLds<NW, T
         const int nbu = (nact + UR - 1) / UR;
         const int last = 31 - __clz(act);
         uint32_t rest = act;  // rows not yet issued (scalar)
-        load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+        load_active_rows<Tr, UR, NSW, kProjStream>(bufA, Wu, rest, last, rowV);
         int b = 0;
 #pragma unroll 1
         for (; b + 2 < nbu; b += 2) {
-            load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+            load_active_rows<Tr, UR, NSW, kProjStream>(bufB, Wu, rest, last, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
             __builtin_amdgcn_sched_barrier(0);
-            load_active_rows<Tr, UR, NSW>(bufA, Wu, rest, last, rowV);
+            load_active_rows<Tr, UR, NSW, kProjStream>(bufA, Wu, rest, last, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (b + 1 < nbu) {
-            load_active_rows<Tr, UR, NSW>(bufB, Wu, rest, last, rowV);
+            load_active_rows<Tr, UR, NSW, kProjStream>(bufB, Wu, rest, last, rowV);
             __builtin_amdgcn_sched_barrier(0);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufA, xr, s_part, wave, b * UR, lane, kidx, owner);
             reduce_batch<Tr, UR, NSW, TT, NW>(bufB, xr, s_part, wave, (b + 1) * UR, lane, kidx, owner);
