@@ -256,9 +256,12 @@ __global__ __launch_bounds__(NW * 64) void k_fused(FusedParams p)
 // reproducible bit for bit.
 // Workgroups after those (only when a union output is requested): one per
 // expert, OR of its pairs' mask words, then the union size and the ascending
-// list of its active neurons.
+// list of its active neurons.  For one token (at most kFcSlots1 slots) the
+// slot ids and every slot's mask words load together and the expert's slot is
+// picked in registers.
 // ---------------------------------------------------------------------------
 constexpr int kFcCols = 64;
+constexpr int kFcSlots1 = 16;  // single-token unions: slots whose mask words load at once
 
 __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
 {
@@ -317,26 +320,50 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
     __shared__ int s_np;
     __shared__ int s_wt[4];
     const int e = blockIdx.x - nyb;
-    if (tid == 0) s_np = 0;
-    __syncthreads();
-    if (e < p.E) {
-        for (int a = tid; a < p.T * p.K; a += blockDim.x)
-            if (p.ids[a] == e) {  // the OR below does not depend on the order
-                const int at = atomicAdd(&s_np, 1);
-                if (at < kFusedMaxT) s_pairs[at] = (a / p.K) * p.slots + a % p.K;
-            }
-    } else {
-        for (int t = tid; t < p.T; t += blockDim.x) s_pairs[t] = t * p.slots + p.K + (e - p.E);
-        if (tid == 0) s_np = p.T;
-    }
-    __syncthreads();
-    const int np = min(s_np, kFusedMaxT);
     const int w0 = 2 * tid;  // words [w0, w0 + 2) of this thread (W <= 512)
     uint32_t u0 = 0u, u1 = 0u;
-    for (int j = 0; j < np; ++j) {
-        const uint32_t *m = p.mw + (size_t)s_pairs[j] * p.W;
-        if (w0 < p.W) u0 |= m[w0];
-        if (w0 + 1 < p.W) u1 |= m[w0 + 1];
+    if (p.T == 1 && p.slots <= kFcSlots1) {
+        // one token: expert e is in at most one slot, and the mask words are
+        // stored by slot, so every slot's words load with the ids (one round
+        // trip instead of a search and then the words)
+        uint32_t v0[kFcSlots1], v1[kFcSlots1];
+        int sid[kFcSlots1];
+#pragma unroll
+        for (int j = 0; j < kFcSlots1; ++j) {
+            v0[j] = v1[j] = 0u;
+            sid[j] = -1;
+            if (j < p.slots) {
+                sid[j] = j < p.K ? p.ids[j] : p.E + (j - p.K);
+                if (w0 < p.W) v0[j] = p.mw[(size_t)j * p.W + w0];
+                if (w0 + 1 < p.W) v1[j] = p.mw[(size_t)j * p.W + w0 + 1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kFcSlots1; ++j)
+            if (sid[j] == e) {
+                u0 |= v0[j];
+                u1 |= v1[j];
+            }
+    } else {
+        if (tid == 0) s_np = 0;
+        __syncthreads();
+        if (e < p.E) {
+            for (int a = tid; a < p.T * p.K; a += blockDim.x)
+                if (p.ids[a] == e) {  // the OR below does not depend on the order
+                    const int at = atomicAdd(&s_np, 1);
+                    if (at < kFusedMaxT) s_pairs[at] = (a / p.K) * p.slots + a % p.K;
+                }
+        } else {
+            for (int t = tid; t < p.T; t += blockDim.x) s_pairs[t] = t * p.slots + p.K + (e - p.E);
+            if (tid == 0) s_np = p.T;
+        }
+        __syncthreads();
+        const int np = min(s_np, kFusedMaxT);
+        for (int j = 0; j < np; ++j) {
+            const uint32_t *m = p.mw + (size_t)s_pairs[j] * p.W;
+            if (w0 < p.W) u0 |= m[w0];
+            if (w0 + 1 < p.W) u1 |= m[w0 + 1];
+        }
     }
     const int cnt = __popc(u0) + __popc(u1);
     const int lane = tid & (kWave - 1), wave = tid / kWave;
