@@ -614,9 +614,14 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 // deterministic).
 // ---------------------------------------------------------------------------
 // NB: slots per thread group whose loads are issued together (1, 2 or 4).
-// Each slot's weight, piece count and first piece depend on (t, slot) alone,
-// so a batch needs one memory latency (and one more for any further pieces).
-template <int NB>
+// Each slot's weight, piece count, compact row and first piece depend on
+// (t, slot) alone, so a batch needs one memory latency for those.  PF: pieces
+// per slot whose loads are issued together; the next PF - 1 pieces of every
+// slot of the batch then take one more latency (a load past the slot's piece
+// count repeats its first piece's address and is not added), and any further
+// pieces one each.  Pieces are added in piece order, so the sum is the same for
+// every PF.
+template <int NB, int PF>
 __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_acc)[3][64])
 {
     const int t = blockIdx.x;
@@ -627,27 +632,42 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
     const int ctg = c4 / (kDownCols / 4);  // the down kernel's column tile of these columns
     float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k0 = g; k0 < p.slots; k0 += 4 * NB) {
-        int np[NB];
+        int np[NB], crow[NB], orow[NB];
         float wk[NB];
         float4 o[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             const int k = min(k0 + 4 * j, p.slots - 1);
-            const int orow = t * p.slots + k;
+            orow[j] = t * p.slots + k;
             const float rw = p.topk_w[(size_t)t * p.K + min(k, p.K - 1)];
             wk[j] = (k < p.K) ? rw : 1.f;
-            np[j] = p.npc[(size_t)orow * p.NCT + ctg];
-            o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)orow * p.H)[c4];
+            np[j] = p.npc[(size_t)orow[j] * p.NCT + ctg];
+            crow[j] = p.cidx[orow[j]];  // -1 for an MFMA expert's pair, which has one piece
+            o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)orow[j] * p.H)[c4];
         }
+        float4 ex[NB][PF > 1 ? PF - 1 : 1];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int kk = 1; kk < PF; ++kk) {
+                const size_t row = kk < np[j] ? (size_t)p.P + (size_t)(kk - 1) * p.G + crow[j] : (size_t)orow[j];
+                ex[j][kk - 1] = reinterpret_cast<const float4 *>(p.partial + row * p.H)[c4];
+            }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             if (k0 + 4 * j >= p.slots) break;
-            const int orow = t * p.slots + k0 + 4 * j;
             float4 v = np[j] > 0 ? o[j] : make_float4(0.f, 0.f, 0.f, 0.f);  // no piece: o = 0
-            const int crow = np[j] > 1 ? p.cidx[orow] : 0;
-            for (int kk = 1; kk < np[j]; ++kk) {
+#pragma unroll
+            for (int kk = 1; kk < PF; ++kk)
+                if (kk < np[j]) {
+                    v.x += ex[j][kk - 1].x;
+                    v.y += ex[j][kk - 1].y;
+                    v.z += ex[j][kk - 1].z;
+                    v.w += ex[j][kk - 1].w;
+                }
+            for (int kk = PF > 1 ? PF : 1; kk < np[j]; ++kk) {
                 const float4 w =
-                    reinterpret_cast<const float4 *>(p.partial + ((size_t)p.P + (size_t)(kk - 1) * p.G + crow) * p.H)[c4];
+                    reinterpret_cast<const float4 *>(p.partial + ((size_t)p.P + (size_t)(kk - 1) * p.G + crow[j]) * p.H)[c4];
                 v.x += w.x;
                 v.y += w.y;
                 v.z += w.z;
@@ -671,18 +691,27 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
     }
 }
 
+template <int PF>
 __global__ __launch_bounds__(256) void k_combine(CombineParams p)
 {
     __shared__ float4 s_acc[3][64];
-    if (p.slots <= 4) combine_body<1>(p, s_acc);
-    else if (p.slots <= 8) combine_body<2>(p, s_acc);
-    else combine_body<4>(p, s_acc);
+    if (p.slots <= 4) combine_body<1, PF>(p, s_acc);
+    else if (p.slots <= 8) combine_body<2, PF>(p, s_acc);
+    else combine_body<4, PF>(p, s_acc);
 }
+
+// Small grids (decode batches) issue 6 pieces of a slot together; large grids
+// (prefill, where most slots have one piece) keep the registers for occupancy.
+constexpr int kCombPrefetchMaxBlocks = 2048;
 
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_combine, dim3(pl.T, pl.H / 256), dim3(256), 0, st, cp);
+    const dim3 grid((unsigned)pl.T, (unsigned)(pl.H / 256));
+    if ((long long)pl.T * (pl.H / 256) <= kCombPrefetchMaxBlocks)
+        hipLaunchKernelGGL(k_combine<6>, grid, dim3(256), 0, st, cp);
+    else
+        hipLaunchKernelGGL(k_combine<1>, grid, dim3(256), 0, st, cp);
     return hipGetLastError();
 }
 
