@@ -138,17 +138,20 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     // read once per pair, mostly from cache while the pairs run together; with
     // small experts and few repeats that costs less than the grouping and the
     // separate down launch save.  Measured (us per call, grouped -> one
-    // launch): Qwen-style T 2/4/8/12/16: 43.6/50.5/67.2/78.5/94.0 ->
-    // 24.0/33.1/52.1/69.4/88.6, T 24: 114 -> 126; DeepSeek-style (2 shared
-    // experts) T 2/4/8: 50.5/62.3/84.8 -> 30.7/44.3/76.4, T 12: 98 -> 113;
+    // launch): Qwen-style T 2/4/8/12/16: 37.9/47.2/66.2/79.0/89.9 ->
+    // 20.9/31.6/54.5/68.8/89.1, T 24: 114 -> 126; DeepSeek-style (2 shared
+    // experts) T 2/4/8: 46.8/60.9/83.0 -> 28.8/46.3/81.8, T 12: 98 -> 113;
     // Mixtral-style (117 MiB of gate per expert) T 2: 122 -> 126.
     {
         const size_t gate_bytes = (size_t)p->Imax * p->H * (p->dtype == MOE_BF16 ? 2 : 4);
-        // (in DENSE mode every row of every pair is streamed, so repeats cost
-        // three times as much: Qwen-style dense T 16 went from 165 to 199 us,
-        // and that mode keeps the limit of 8)
-        const bool small = gate_bytes <= ((size_t)16 << 20) &&
-                           (T <= 8 || (mode != MOE_DENSE && p->S == 0 && T <= kFusedMaxT && T * p->K <= p->E));
+        // In DENSE mode every row of every pair is streamed, so repeated
+        // experts cost three times as much: Qwen-style dense T 2/4/8
+        // 48.8/68.1/105.9 -> 35.1/58.1/109.1, DeepSeek-style (whose shared
+        // experts repeat for every token) 62.3/85.1/112.9 -> 49.4/90.1/174.1.
+        const bool small =
+            gate_bytes <= ((size_t)16 << 20) &&
+            (mode == MOE_DENSE ? (T <= 2 || (p->S == 0 && T <= 4))
+                               : (T <= 8 || (p->S == 0 && T <= kFusedMaxT && T * p->K <= p->E)));
         p->fused = !calib && !p->topk && T >= 1 && (T == 1 || small) ? 1 : 0;
     }
 
