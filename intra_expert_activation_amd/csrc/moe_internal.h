@@ -220,7 +220,6 @@ hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEven
 #if defined(__HIPCC__)
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// bf16 weights/activations: 8 elements per 16-byte vector.
 // Loads of weight rows that a call streams once: nontemporal, so the caches do
 // not keep them.  Whole 4 KiB rows read this way measured 6.8-7.0 TB/s on
 // MI355X against 6.0-6.1 TB/s with ordinary loads (1 GiB, 512 to 4096
@@ -244,6 +243,7 @@ __device__ __forceinline__ float4 load_stream(const float4 *p)
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// bf16 weights/activations: 8 elements per 16-byte vector.
 struct BF16 {
     using V = uint4;
     static constexpr int kEpl = 8;
