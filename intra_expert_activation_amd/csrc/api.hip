@@ -128,6 +128,19 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
         const long long g = p->use_mfma ? (long long)p->EX * (p->nm - 1) : (long long)p->P;
         p->G = (int)(g < p->P ? g : p->P);
     }
+    // MFMA down: a workgroup per (item, 128 columns) walks the expert's
+    // neuron tiles one staged tile at a time, so with few items (a few wide
+    // experts: 8 experts x 224 neuron tiles at 128-256 tokens) the grid holds
+    // a few hundred long serial walks.  Splitting the tiles into segments, one
+    // partial sum each (added by the combine in segment order), fills the
+    // device.
+    p->NKS = 1;
+    if (p->use_mfma) {
+        const long long units = (long long)p->max_items * (p->H / kMfmaDownCols);
+        while (p->NKS < kMfmaDownMaxSegs && units * p->NKS < kMfmaDownUnits &&
+               p->NT >= kMfmaDownMinTiles * (p->NKS + 1))
+            ++p->NKS;
+    }
 
     // one-launch decode path: single-token batches (every expert has one
     // pair), and small batches of layers whose experts' gate matrices hold at
@@ -176,11 +189,14 @@ moe_status make_plan(const moe_shape *s, int mode, int calib_tokens, Plan *p)
     p->off_ucount = take((size_t)p->EX * 4);
     p->off_npc = take(calib ? 0 : (size_t)p->P * p->NCT * 4);
     p->off_h = take(((size_t)p->A * p->I + (size_t)p->S * T * p->Is) * 4);
-    // down outputs: piece 0 of every pair [P, H]; the later pieces only for
-    // the GEMV experts' pairs [KMAX - 1, G, H] (the one-launch path keeps its
-    // chunk partial rows [P, C, H] here instead)
+    // down outputs: piece 0 of every pair [P, H]; the later pieces of the
+    // GEMV experts' pairs [KMAX - 1, G, H]; the later segments of the MFMA
+    // experts' pairs [NKS - 1, P, H] (the one-launch path keeps its chunk
+    // partial rows [P, C, H] here instead)
     p->off_partial = take(calib ? 0
-                                : (p->fused ? (size_t)p->C * p->P : (size_t)p->P + (size_t)(p->KMAX - 1) * p->G) *
+                                : (p->fused ? (size_t)p->C * p->P
+                                            : (size_t)p->P + (size_t)(p->KMAX - 1) * p->G +
+                                                  (size_t)(p->NKS - 1) * p->P) *
                                       p->H * 4);
     p->off_cidx = take(calib ? 0 : (size_t)p->P * 4);
     p->off_taus = take((size_t)(2 + p->EX) * 4);
@@ -313,7 +329,8 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
         fp.y = a->y;
         fp.T = pl.T; fp.H = pl.H; fp.E = pl.E; fp.I = pl.I; fp.Is = pl.Is; fp.S = pl.S; fp.K = pl.K;
         fp.slots = pl.slots; fp.P = pl.P; fp.C = pl.C; fp.W = pl.W; fp.Imax = pl.Imax; fp.renorm = pl.renorm;
-        return launch_fused(pl, fp, mode, ev_begin, ev_end, stream)
+        KernelEvents kev{ev_begin, ev_end};
+        return launch_fused(pl, fp, mode, &kev, stream)
                        == hipSuccess
                    ? MOE_OK
                    : MOE_ERR_HIP;
@@ -360,25 +377,27 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
     mp.union_idx = a->union_idx; mp.union_cnt = a->union_cnt;
     mp.H = pl.H; mp.E = pl.E; mp.I = pl.I; mp.Is = pl.Is; mp.S = pl.S; mp.W = pl.W; mp.Imax = pl.Imax;
     mp.slots = pl.slots; mp.NT = pl.NT; mp.max_items = pl.max_items;
+    mp.NKS = pl.NKS; mp.P = pl.P; mp.mbase = (size_t)pl.P + (size_t)(pl.KMAX - 1) * pl.G;
 
-    // the events bracket the expert projection (gate, score, mask, up) of both paths
-    if (ev_begin && hipEventRecord(ev_begin, stream) != hipSuccess) return MOE_ERR_HIP;
+    // the events time the expert projection (gate, score, mask, up): the
+    // kernel itself, or in top-k mode its three launches
     if (pl.topk) {
         // every pair's gate scores, the per-pair selection of the budget
         // largest, then the projection under those masks (up and h; the gate
         // is not read again)
-        if (launch_proj(pl, pp, mp, kModeScore, stream) != hipSuccess) return MOE_ERR_HIP;
+        const KernelEvents first{ev_begin, nullptr}, last{nullptr, ev_end};
+        if (launch_proj(pl, pp, mp, kModeScore, stream, &first) != hipSuccess) return MOE_ERR_HIP;
         TopkParams tp{};
         tp.a = h; tp.counts = counts; tp.offsets = offsets; tp.pair_tok = pair_tok; tp.pair_slot = pair_slot;
         tp.ids = ids; tp.pmask = ws_at<uint32_t>(ws, pl.off_mw);
         tp.E = pl.E; tp.I = pl.I; tp.Is = pl.Is; tp.K = pl.K; tp.A = pl.A; tp.W = pl.W; tp.budget = a->neuron_budget;
         if (launch_topk_select(pl, tp, stream) != hipSuccess) return MOE_ERR_HIP;
         pp.pmask = tp.pmask;
-        if (launch_proj(pl, pp, mp, kModeMasked, stream) != hipSuccess) return MOE_ERR_HIP;
-    } else if (launch_proj(pl, pp, mp, mode, stream) != hipSuccess) {
-        return MOE_ERR_HIP;
+        if (launch_proj(pl, pp, mp, kModeMasked, stream, &last) != hipSuccess) return MOE_ERR_HIP;
+    } else {
+        const KernelEvents kev{ev_begin, ev_end};
+        if (launch_proj(pl, pp, mp, mode, stream, &kev) != hipSuccess) return MOE_ERR_HIP;
     }
-    if (ev_end && hipEventRecord(ev_end, stream) != hipSuccess) return MOE_ERR_HIP;
 
     DownParams dp{};
     dp.wd = a->w_down; dp.swd = a->ws_down; dp.h = h;
@@ -396,6 +415,7 @@ static moe_status ffn_call(const moe_shape *shape, int32_t mode, const moe_ffn_a
     CombineParams cp{};
     cp.partial = partial; cp.cidx = gp.cidx; cp.topk_w = w; cp.npc = npc; cp.y = a->y;
     cp.T = pl.T; cp.H = pl.H; cp.K = pl.K; cp.slots = pl.slots; cp.P = pl.P; cp.NCT = pl.NCT; cp.G = pl.G;
+    cp.mbase = mp.mbase;
     if (launch_combine(pl, cp, stream) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -579,7 +579,7 @@ static hipError_t launch_down_m(const Plan &pl, const DownParams &dp_in, const M
     if constexpr (std::is_same<Tr, BF16>::value) {
         if (pl.use_mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
             dp.GD = down_groups(pl, resident_blocks<k_down_bf16<MODE>>());
-            const int grid = dp.GD + round8_down((long long)pl.max_items * (pl.H / kTC));
+            const int grid = dp.GD + round8_down((long long)pl.max_items * (pl.H / kTC) * pl.NKS);
             hipLaunchKernelGGL((k_down_bf16<MODE>), dim3(grid), dim3(256), 0, st, dp, mp);
             return hipGetLastError();
         }
@@ -608,8 +608,9 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 // o of a GEMV expert's pair is the sum, in piece order, of the partial sums of
 // the pieces its group (token tile, column tile) was cut into (npc of them:
 // piece 0 at the pair's (token, slot) row, the others at its compact row);
-// an MFMA expert writes piece 0 only.  A workgroup covers one token and one 256-column tile:
-// 64 column quads x 4 thread groups; group g adds the slots k with k % 4 == g,
+// an MFMA expert's pair has one piece per segment of its neuron tiles (piece 0
+// as above, the others by (token, slot) row after the GEMV pieces).  A
+// workgroup covers one token and one 256-column tile: 64 column quads x 4 thread groups; group g adds the slots k with k % 4 == g,
 // and the 4 group sums meet in LDS in a fixed order (so the result is
 // deterministic).
 // ---------------------------------------------------------------------------
@@ -621,6 +622,13 @@ hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &m
 // count repeats its first piece's address and is not added), and any further
 // pieces one each.  Pieces are added in piece order, so the sum is the same for
 // every PF.
+// Row of piece k >= 1 of the pair at (token, slot) row orow: a GEMV expert's
+// pair at its compact row crow, an MFMA expert's pair (crow -1) by segment.
+__device__ __forceinline__ size_t piece_row(const CombineParams &p, int k, int crow, int orow)
+{
+    return crow >= 0 ? (size_t)p.P + (size_t)(k - 1) * p.G + crow : p.mbase + (size_t)(k - 1) * p.P + orow;
+}
+
 template <int NB, int PF>
 __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_acc)[3][64])
 {
@@ -642,7 +650,7 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
             const float rw = p.topk_w[(size_t)t * p.K + min(k, p.K - 1)];
             wk[j] = (k < p.K) ? rw : 1.f;
             np[j] = p.npc[(size_t)orow[j] * p.NCT + ctg];
-            crow[j] = p.cidx[orow[j]];  // -1 for an MFMA expert's pair, which has one piece
+            crow[j] = p.cidx[orow[j]];  // -1 for an MFMA expert's pair
             o[j] = reinterpret_cast<const float4 *>(p.partial + (size_t)orow[j] * p.H)[c4];
         }
         float4 ex[NB][PF > 1 ? PF - 1 : 1];
@@ -650,7 +658,7 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
         for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int kk = 1; kk < PF; ++kk) {
-                const size_t row = kk < np[j] ? (size_t)p.P + (size_t)(kk - 1) * p.G + crow[j] : (size_t)orow[j];
+                const size_t row = kk < np[j] ? piece_row(p, kk, crow[j], orow[j]) : (size_t)orow[j];
                 ex[j][kk - 1] = reinterpret_cast<const float4 *>(p.partial + row * p.H)[c4];
             }
 #pragma unroll
@@ -666,8 +674,7 @@ __device__ __forceinline__ void combine_body(const CombineParams &p, float4 (&s_
                     v.w += ex[j][kk - 1].w;
                 }
             for (int kk = PF > 1 ? PF : 1; kk < np[j]; ++kk) {
-                const float4 w =
-                    reinterpret_cast<const float4 *>(p.partial + ((size_t)p.P + (size_t)(kk - 1) * p.G + crow[j]) * p.H)[c4];
+                const float4 w = reinterpret_cast<const float4 *>(p.partial + piece_row(p, kk, crow[j], orow[j]) * p.H)[c4];
                 v.x += w.x;
                 v.y += w.y;
                 v.z += w.z;

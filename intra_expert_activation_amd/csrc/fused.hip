@@ -387,46 +387,48 @@ __global__ __launch_bounds__(256) void k_fcombine(FusedParams p)
 
 // ---------------------------------------------------------------------------
 template <class Tr, int NW, int NSW, bool NT>
-static hipError_t launch_fused_nt(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
+static hipError_t launch_fused_nt(const Plan &pl, const FusedParams &fp, int mode, const KernelEvents &ev,
+                                  hipStream_t st)
 {
     const dim3 grid((unsigned)(pl.P * pl.C + pl.T));  // + one routing-store workgroup per token
     if (mode == MOE_DENSE)
-        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_DENSE, NT>), grid, dim3(NW * kWave), 0, st, fp);
+        launch_timed(k_fused<Tr, NW, NSW, MOE_DENSE, NT>, grid, dim3(NW * kWave), st, ev.begin, ev.end, fp);
     else
-        hipLaunchKernelGGL((k_fused<Tr, NW, NSW, MOE_SPARSE, NT>), grid, dim3(NW * kWave), 0, st, fp);
+        launch_timed(k_fused<Tr, NW, NSW, MOE_SPARSE, NT>, grid, dim3(NW * kWave), st, ev.begin, ev.end, fp);
     return hipGetLastError();
 }
 
 template <class Tr, int NW, int NSW>
-static hipError_t launch_fused_ns(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
+static hipError_t launch_fused_ns(const Plan &pl, const FusedParams &fp, int mode, const KernelEvents &ev,
+                                  hipStream_t st)
 {
-    return pl.T == 1 ? launch_fused_nt<Tr, NW, NSW, true>(pl, fp, mode, st)
-                     : launch_fused_nt<Tr, NW, NSW, false>(pl, fp, mode, st);
+    return pl.T == 1 ? launch_fused_nt<Tr, NW, NSW, true>(pl, fp, mode, ev, st)
+                     : launch_fused_nt<Tr, NW, NSW, false>(pl, fp, mode, ev, st);
 }
 
 template <class Tr>
-static hipError_t launch_fused_tr(const Plan &pl, const FusedParams &fp, int mode, hipStream_t st)
+static hipError_t launch_fused_tr(const Plan &pl, const FusedParams &fp, int mode, const KernelEvents &ev,
+                                  hipStream_t st)
 {
     switch (pl.NS) {  // as the expert projection: NS vectors per lane per row over up to 4 wavefronts
-    case 1: return launch_fused_ns<Tr, 1, 1>(pl, fp, mode, st);
-    case 2: return launch_fused_ns<Tr, 2, 1>(pl, fp, mode, st);
-    case 4: return launch_fused_ns<Tr, 4, 1>(pl, fp, mode, st);
-    case 8: return launch_fused_ns<Tr, 4, 2>(pl, fp, mode, st);
-    case 16: return launch_fused_ns<Tr, 4, 4>(pl, fp, mode, st);
+    case 1: return launch_fused_ns<Tr, 1, 1>(pl, fp, mode, ev, st);
+    case 2: return launch_fused_ns<Tr, 2, 1>(pl, fp, mode, ev, st);
+    case 4: return launch_fused_ns<Tr, 4, 1>(pl, fp, mode, ev, st);
+    case 8: return launch_fused_ns<Tr, 4, 2>(pl, fp, mode, ev, st);
+    case 16: return launch_fused_ns<Tr, 4, 4>(pl, fp, mode, ev, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEvent_t ev_begin, hipEvent_t ev_end,
-                        hipStream_t st)
+hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, const KernelEvents *ev, hipStream_t st)
 {
     if (pl.T <= 0) return hipSuccess;
     if (pl.T > kFusedMaxT || pl.C != pl.W || pl.H % kFcCols != 0) return hipErrorInvalidValue;
-    if (ev_begin && hipEventRecord(ev_begin, st) != hipSuccess) return hipErrorInvalidValue;
-    hipError_t e = pl.dtype == MOE_BF16 ? launch_fused_tr<BF16>(pl, fp, mode, st)
-                                        : launch_fused_tr<F32>(pl, fp, mode, st);
-    if (e != hipSuccess) return e;
-    if (ev_end && hipEventRecord(ev_end, st) != hipSuccess) return hipErrorInvalidValue;
+    const KernelEvents none{};
+    const KernelEvents &e = ev ? *ev : none;
+    hipError_t err = pl.dtype == MOE_BF16 ? launch_fused_tr<BF16>(pl, fp, mode, e, st)
+                                          : launch_fused_tr<F32>(pl, fp, mode, e, st);
+    if (err != hipSuccess) return err;
     const int unions = (fp.union_idx || fp.union_cnt) ? pl.EX : 0;
     hipLaunchKernelGGL(k_fcombine, dim3((unsigned)(pl.T * (pl.H / kFcCols) + unions)), dim3(256), 0, st, fp);
     return hipGetLastError();

@@ -45,12 +45,13 @@ __global__ __launch_bounds__(256, 3) void k_proj_mfma(MfmaParams p)
 
 static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
 
-hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t st)
+hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t st, hipEvent_t ev_begin,
+                            hipEvent_t ev_end)
 {
     if (!pl.use_mfma) return hipSuccess;
     const dim3 grid(round8((long long)pl.max_pairs * pl.NT)), block(256);
-    if (mode == MOE_DENSE) hipLaunchKernelGGL(k_proj_mfma<MOE_DENSE>, grid, block, 0, st, mp);
-    else hipLaunchKernelGGL(k_proj_mfma<MOE_SPARSE>, grid, block, 0, st, mp);
+    if (mode == MOE_DENSE) launch_timed(k_proj_mfma<MOE_DENSE>, grid, block, st, ev_begin, ev_end, mp);
+    else launch_timed(k_proj_mfma<MOE_SPARSE>, grid, block, st, ev_begin, ev_end, mp);
     return hipGetLastError();
 }
 

@@ -21,11 +21,14 @@
 //               and h = m ? a*u : 0 of those rows stored compacted
 //               [64 tokens][active rows] as a bf16 pair (hi + lo = h to
 //               ~2^-17) so the down product keeps fp32-level accuracy.
-//  k_down_mfma  (item, 128-column tile): O = sum over neuron tiles of
+//  k_down_mfma  (item, segment of the neuron tiles, 128-column tile):
+//               O = sum over the segment's neuron tiles of
 //               H_tile[64 x active] * W_down[active rows, 128 cols]; the
 //               neuron-major down rows are staged row-major in LDS and read
 //               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
-//               output per pair (no split).
+//               partial output per pair and segment; the plan uses one
+//               segment unless few items leave the device short of
+//               workgroups (a few wide experts).
 // Work indices are remapped so that each XCD (8 per MI355X, each with its own
 // L2) runs a contiguous range of the work units that exist.
 #pragma once
@@ -41,7 +44,7 @@ constexpr int kTM = 64;                 // tokens per tile
 constexpr int kTN = 64;                 // neurons per tile
 constexpr int kKC = 64;                 // K chunk staged in LDS
 constexpr int kRow = kKC + 8;           // padded LDS row (bf16 elements), 144 bytes
-constexpr int kTC = 128;                // output columns per down tile
+constexpr int kTC = kMfmaDownCols;      // output columns per down tile (128)
 
 // Logical work index of workgroup b when nvalid work units exist (known on
 // the device only), or -1.  Consecutive workgroups are dispatched round-robin
@@ -363,9 +366,13 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
 
     const int nct = p.H / kTC;
     const int nitems = p.hdr[1];
-    const int L = xcd_remap(b, nitems * nct);
+    const int L = xcd_remap(b, nitems * p.NKS * nct);
     if (L < 0) return;
-    const int item = L / nct, ct = L - item * nct;  // item-major: the item's h tiles stay in L2 across its column tiles
+    // item-major, then segment: the h tiles of an (item, segment) stay in L2
+    // across its column tiles
+    const int item = L / (p.NKS * nct);
+    const int ks = (L - item * p.NKS * nct) / nct;
+    const int ct = L - (item * p.NKS + ks) * nct;
     const int code = p.items[item];
     const int xe = code >> 16, tile = code & 0xffff;
     const bool shared = xe >= p.E;
@@ -377,6 +384,9 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
     const int NTe = (Ie + kTN - 1) / kTN;
+    // this workgroup's segment of the neuron tiles: [ts0, ts1)
+    const int per = (NTe + p.NKS - 1) / p.NKS;
+    const int ts0 = min(NTe, ks * per), ts1 = min(NTe, ts0 + per);
     // this thread's pieces: h rows tid / 8 and 32 + tid / 8 (16 bytes at
     // column 8 (tid % 8)); down rows tid / 16 + 16 i (16 bytes at column
     // 8 (tid % 16)), i < 4
@@ -388,8 +398,8 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
         S.sRow[tid] = p.pair_tok[pr] * p.slots + p.pair_slot[pr];
     }
     f32x16_t acc[2] = {};
-    for (int seg = 0; seg < NTe; seg += kDSeg) {
-        const int ns = min(kDSeg, NTe - seg);
+    for (int seg = ts0; seg < ts1; seg += kDSeg) {
+        const int ns = min(kDSeg, ts1 - seg);
         __syncthreads();  // the previous segment's lists are no longer read
         for (int q = tid; q < ns * kTN; q += 256) {
             const int t = q / kTN, c = q - t * kTN;
@@ -451,19 +461,23 @@ __device__ __forceinline__ void mfma_down_body(const MfmaParams &p, MfmaDownLds 
             cur = nxt;
         }
     }
+    // segment 0 at the pair's (token, slot) row, segment k >= 1 at row
+    // mbase + (k - 1) P + (token, slot) row
+    const size_t rbase = ks == 0 ? 0 : p.mbase + (size_t)(ks - 1) * p.P;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int m = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int col = c0 + 64 * wn + 32 * nb + (lane & 31);
-            if (m < mt) p.partial[(size_t)S.sRow[m] * H + col] = acc[nb][r];
+            if (m < mt) p.partial[(rbase + S.sRow[m]) * H + col] = acc[nb][r];
         }
-    // one piece per pair and 1024-column tile (recorded by its first 128-column tile)
-    if (c0 % 1024 == 0 && tid < mt) p.npc[(size_t)S.sRow[tid] * p.NCT + c0 / 1024] = 1;
+    // NKS pieces per pair and 1024-column tile (recorded by the first
+    // segment's first 128-column tile)
+    if (ks == 0 && c0 % 1024 == 0 && tid < mt) p.npc[(size_t)S.sRow[tid] * p.NCT + c0 / 1024] = p.NKS;
 
     // the expert's union list (complete: every projection tile has finished)
-    if (tile == 0 && ct == 0 && (p.union_idx || p.union_cnt)) {
+    if (tile == 0 && ct == 0 && ks == 0 && (p.union_idx || p.union_cnt)) {
         const int nw = Ie / 32;
         const uint32_t *uw = p.union_words + (size_t)xe * p.W;
         const int per = (nw + 255) / 256;

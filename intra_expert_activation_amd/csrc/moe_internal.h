@@ -2,6 +2,7 @@
 // kernel parameter blocks and small device helpers.  Not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -19,6 +20,14 @@ constexpr int kMfmaTokens = 64;    // token tile of the MFMA path
 constexpr int kGroupBlock = 2048;  // routed pairs per grouping workgroup when the batch has more
 constexpr int kMfmaMinPairs = 16;  // pair-count threshold of the MFMA path
 constexpr int kFusedMaxT = 16;     // most tokens of a batch on the one-launch decode path
+constexpr int kMfmaDownCols = 128; // output columns of an MFMA down workgroup
+// The MFMA down splits each expert's neuron tiles into up to kMfmaDownMaxSegs
+// segments (one partial sum each) while its grid bound, items x column tiles
+// x segments, stays below kMfmaDownUnits; every segment keeps at least
+// kMfmaDownMinTiles neuron tiles.
+constexpr int kMfmaDownUnits = 1024;
+constexpr int kMfmaDownMaxSegs = 4;
+constexpr int kMfmaDownMinTiles = 8;
 
 // ---------------------------------------------------------------------------
 // Launch plan: every size a kernel grid or the workspace depends on.  It is a
@@ -51,6 +60,7 @@ struct Plan {
     int max_items;   // upper bound on (expert, 64-token tile) work items
     int max_pairs;   // upper bound on pairs of them (the MFMA projection's items)
     int G;           // upper bound on the pairs of GEMV experts (rows of the down pieces after the first)
+    int NKS;         // segments of an MFMA expert's neuron tiles in the down product (pieces of its pairs)
     // one-launch decode path (small batches): every (pair, 32-row chunk)
     // runs routing, gate, mask, up and down; a second launch combines
     int fused;
@@ -139,6 +149,7 @@ struct CombineParams {
     const float *topk_w;
     const int32_t *npc;   // as DownParams
     float *y;
+    size_t mbase;         // as MfmaParams: pieces after the first of an MFMA pair (cidx -1)
     int T, H, K, slots, P, NCT, G;
 };
 
@@ -150,10 +161,11 @@ struct MfmaParams {
     int32_t *nact;        // active rows per (item, neuron tile)
     uint8_t *list;        // their offsets within the tile, ascending
     uint32_t *mask_bits, *union_words;
-    float *partial;       // as DownParams (piece 0 only)
+    float *partial;       // as DownParams; piece k >= 1 of a pair at row mbase + (k - 1) P + (t * slots + slot)
     int32_t *npc;         // as DownParams
     int32_t *union_idx, *union_cnt;
-    int H, E, I, Is, S, W, Imax, slots, NT, max_items, max_pairs, NCT;
+    size_t mbase;         // first row of the MFMA pairs' pieces after the first
+    int H, E, I, Is, S, W, Imax, slots, NT, max_items, max_pairs, NCT, NKS, P;
 };
 
 // One-launch decode path.  Pair p = t * slots + slot; chunk c = rows
@@ -191,6 +203,24 @@ struct SelectParams {
 // ---------------------------------------------------------------------------
 // Host-side launchers (each enqueues on `stream` and returns hipGetLastError)
 // ---------------------------------------------------------------------------
+// Optional timing of a launch: the kernel is dispatched by
+// hipExtLaunchKernelGGL, whose start and stop events take the kernel's own
+// begin and end times (events recorded around hipLaunchKernelGGL also count
+// the dispatch, 2-4 us on the expert projection).  A null pointer, or null
+// members, launch without events.
+struct KernelEvents {
+    hipEvent_t begin = nullptr, end = nullptr;
+};
+
+template <class F, class... Args>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, hipEvent_t begin, hipEvent_t end,
+                         Args... args)
+{
+    if (begin || end)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, begin, end, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 hipError_t launch_route(const float *logits, int T, int E, int K, int renorm, int32_t *ids,
                         float *w, hipStream_t stream);
 // Routing then grouping of gp.T tokens (ids/w: the routing outputs, also gp.ids).
@@ -203,15 +233,18 @@ constexpr int kModeScore = 3;
 constexpr int kModeMasked = 4;
 // MFMA workgroups (experts with >= nm pairs) run in the same launch for bf16
 // layers with 256-thread GEMV workgroups, else in a second launch.
-hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t stream);
+// ev (optional) times the launch or launches of this call.
+hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t stream,
+                       const KernelEvents *ev = nullptr);
 hipError_t launch_down(const Plan &pl, const DownParams &dp, const MfmaParams &mp, int mode, hipStream_t stream);
 hipError_t launch_combine(const Plan &pl, const CombineParams &cp, hipStream_t stream);
 hipError_t launch_select(const Plan &pl, const SelectParams &sp, float *tau_out, hipStream_t stream);
 hipError_t launch_topk_select(const Plan &pl, const TopkParams &tp, hipStream_t stream);
-hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream);
-// The one-launch decode path and its combine; the events (optional) bracket
-// the first launch.
-hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, hipEvent_t ev_begin, hipEvent_t ev_end,
+hipError_t launch_proj_mfma(const Plan &pl, const MfmaParams &mp, int mode, hipStream_t stream,
+                            hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+// The one-launch decode path and its combine; ev (optional) times the first
+// launch.
+hipError_t launch_fused(const Plan &pl, const FusedParams &fp, int mode, const KernelEvents *ev,
                         hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -293,7 +293,8 @@ __global__ __launch_bounds__(256, 3) void k_proj_bf16(ProjParams p, MfmaParams m
 static int round8(long long v) { return (int)((v + 7) / 8 * 8); }
 
 template <class Tr, int NW, int NSW, int TT, int MODE>
-static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, hipStream_t st)
+static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, hipStream_t st,
+                                const KernelEvents &ev)
 {
     const bool mfma = (MODE == MOE_SPARSE || MODE == MOE_DENSE) && pl.use_mfma;
     // one 16-byte vector per lane per row only: with more, the merged kernel's
@@ -303,58 +304,67 @@ static hipError_t launch_proj_m(const Plan &pl, const ProjParams &pp, const Mfma
         if (mfma) {  // the merged kernel carries the MFMA tiles' LDS; only when they can exist
             const int mfma_blocks = round8((long long)pl.max_pairs * pl.NT);
             const int grid = mfma_blocks + pl.max_touched * pl.C;
-            hipLaunchKernelGGL((k_proj_bf16<NSW, TT, MODE>), dim3(grid), dim3(256), 0, st, pp, mp, mfma_blocks);
+            launch_timed(k_proj_bf16<NSW, TT, MODE>, dim3(grid), dim3(256), st, ev.begin, ev.end, pp, mp,
+                         mfma_blocks);
             return hipGetLastError();
         }
     }
     {
-        hipLaunchKernelGGL((k_proj<Tr, NW, NSW, TT, MODE>), dim3(pl.max_touched * pl.C), dim3(NW * kWave), 0, st, pp);
+        // with a second (MFMA) launch, the stop event goes with that one
+        launch_timed(k_proj<Tr, NW, NSW, TT, MODE>, dim3(pl.max_touched * pl.C), dim3(NW * kWave), st, ev.begin,
+                     mfma ? nullptr : ev.end, pp);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess || !mfma) return e;
-        return launch_proj_mfma(pl, mp, MODE, st);
+        return launch_proj_mfma(pl, mp, MODE, st, nullptr, ev.end);
     }
 }
 
 template <class Tr, int NW, int NSW, int TT>
-static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
+static hipError_t launch_proj_t(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st,
+                                const KernelEvents &ev)
 {
-    if (mode == MOE_SPARSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_SPARSE>(pl, pp, mp, st);
-    if (mode == MOE_DENSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_DENSE>(pl, pp, mp, st);
-    if (mode == kModeMasked) return launch_proj_m<Tr, NW, NSW, TT, kModeMasked>(pl, pp, mp, st);
-    return launch_proj_m<Tr, NW, NSW, TT, kModeScore>(pl, pp, mp, st);
+    if (mode == MOE_SPARSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_SPARSE>(pl, pp, mp, st, ev);
+    if (mode == MOE_DENSE) return launch_proj_m<Tr, NW, NSW, TT, MOE_DENSE>(pl, pp, mp, st, ev);
+    if (mode == kModeMasked) return launch_proj_m<Tr, NW, NSW, TT, kModeMasked>(pl, pp, mp, st, ev);
+    return launch_proj_m<Tr, NW, NSW, TT, kModeScore>(pl, pp, mp, st, ev);
 }
 
 template <class Tr, int NW, int NSW>
-static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
+static hipError_t launch_proj_ns(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st,
+                                 const KernelEvents &ev)
 {
     switch (pl.TT) {  // the largest token tile
-    case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mp, mode, st);
-    case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mp, mode, st);
-    case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mp, mode, st);
-    case 8: if constexpr (NSW <= 2) return launch_proj_t<Tr, NW, NSW, 8>(pl, pp, mp, mode, st); break;
+    case 1: return launch_proj_t<Tr, NW, NSW, 1>(pl, pp, mp, mode, st, ev);
+    case 2: return launch_proj_t<Tr, NW, NSW, 2>(pl, pp, mp, mode, st, ev);
+    case 4: return launch_proj_t<Tr, NW, NSW, 4>(pl, pp, mp, mode, st, ev);
+    case 8: if constexpr (NSW <= 2) return launch_proj_t<Tr, NW, NSW, 8>(pl, pp, mp, mode, st, ev); break;
     }
     return hipErrorInvalidValue;
 }
 
 template <class Tr>
-static hipError_t launch_proj_tr(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
+static hipError_t launch_proj_tr(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st,
+                                 const KernelEvents &ev)
 {
     // NS 16-byte vectors per lane per row, split over up to 4 wavefronts
     switch (pl.NS) {
-    case 1: return launch_proj_ns<Tr, 1, 1>(pl, pp, mp, mode, st);
-    case 2: return launch_proj_ns<Tr, 2, 1>(pl, pp, mp, mode, st);
-    case 4: return launch_proj_ns<Tr, 4, 1>(pl, pp, mp, mode, st);
-    case 8: return launch_proj_ns<Tr, 4, 2>(pl, pp, mp, mode, st);
-    case 16: return launch_proj_ns<Tr, 4, 4>(pl, pp, mp, mode, st);
+    case 1: return launch_proj_ns<Tr, 1, 1>(pl, pp, mp, mode, st, ev);
+    case 2: return launch_proj_ns<Tr, 2, 1>(pl, pp, mp, mode, st, ev);
+    case 4: return launch_proj_ns<Tr, 4, 1>(pl, pp, mp, mode, st, ev);
+    case 8: return launch_proj_ns<Tr, 4, 2>(pl, pp, mp, mode, st, ev);
+    case 16: return launch_proj_ns<Tr, 4, 4>(pl, pp, mp, mode, st, ev);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st)
+hipError_t launch_proj(const Plan &pl, const ProjParams &pp, const MfmaParams &mp, int mode, hipStream_t st,
+                       const KernelEvents *ev)
 {
     if (pl.T <= 0) return hipSuccess;
-    return pl.dtype == MOE_BF16 ? launch_proj_tr<BF16>(pl, pp, mp, mode, st)
-                                : launch_proj_tr<F32>(pl, pp, mp, mode, st);
+    const KernelEvents none{};
+    const KernelEvents &e = ev ? *ev : none;
+    return pl.dtype == MOE_BF16 ? launch_proj_tr<BF16>(pl, pp, mp, mode, st, e)
+                                : launch_proj_tr<F32>(pl, pp, mp, mode, st, e);
 }
 
 }  // namespace moe
