@@ -21,11 +21,13 @@
 //               and h = m ? a*u : 0 of those rows stored compacted
 //               [64 tokens][active rows] as a bf16 pair (hi + lo = h to
 //               ~2^-17) so the down product keeps fp32-level accuracy.
-//  down body   (item, 128-column tile), in the merged down kernel: O = sum over neuron tiles of
-//               H_tile[64 x active] * W_down[active rows, 128 cols]; the
+//  down body   (item, segment of the neuron tiles, 128-column tile), in the
+//               merged down kernel: O = sum over the segment's neuron tiles
+//               of H_tile[64 x active] * W_down[active rows, 128 cols]; the
 //               neuron-major down rows are staged row-major in LDS and read
 //               transposed (ds_read_b64_tr_b16) as the MFMA B operand.  One
-//               output per pair (no split).
+//               partial output per pair and segment (one segment unless few
+//               items leave the device short of workgroups).
 // Work indices are remapped so that each XCD (8 per MI355X, each with its own
 // L2) runs a contiguous range of the work units that exist.
 #include "mfma_body.h"
