@@ -119,6 +119,29 @@ def test_deepseek_block_grouping(T):
     print(f"T={T} err={s['err']:.2e} band={s['band']} flips={s['flips']}")
 
 
+# ---------------------------------------------------------------------------
+# MFMA down split into neuron-tile segments, with experts of two widths: a
+# DeepSeek-style layer cut to H 512, 8 routed experts of I 1024 (16 neuron
+# tiles, so the plan splits them into 2 segments) and 2 shared experts of
+# I 512 (8 tiles), T 40 / 64 / 100 (every expert on the MFMA path; at 64 and
+# 100 some take two token tiles).  Segment k of a pair is partial output k,
+# added by the combine; every row is checked against the oracle.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [40, 64, 100])
+def test_mfma_down_segments_mixed_widths(T):
+    c, L = cached_layer(4, (("H", 512), ("E", 8), ("I", 1024), ("I_shared", 512)))
+    DL = layer_to_device(L)
+    x, logits = synth.make_tokens(c, 2, 100)
+    x, logits = x[:T], logits[:T]
+    tau = _tau(L, c, 0.8)
+    s = check_layer(L, DL, x, logits, tau, tol=TOL_BF16)
+    assert 0.05 < s["active"] < 0.5
+    check_layer(L, DL, x, logits, None, mode=moe.MOE_DENSE, tol=TOL_BF16)
+    sp = gpu_ffn(DL, x, logits, 0.0)
+    de = gpu_ffn(DL, x, logits, None, mode=moe.MOE_DENSE)
+    assert np.array_equal(sp["y"], de["y"])
+
+
 @pytest.mark.parametrize("T", [1, 8, 40])
 def test_deepseek_shared_kept_dense(T):
     # the policy of keeping the shared experts dense (their neurons matter
